@@ -1,0 +1,144 @@
+"""CPU oracle for the Muon optimizer's hot path: Nesterov momentum, then quintic
+Newton-Schulz orthogonalisation (NS5) run in bfloat16.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The GPU
+library shares no code with it and never calls it.
+
+Source: Synced (机器之心) report on Modded-NanoGPT, section "Muon optimizer":
+  * the printed function ``zeroth_power_via_newtonschulz5(G, steps=5, eps=1e-7)``
+    fixes the coefficients (a, b, c) = (3.4445, -4.7750, 2.0315), the
+    normalisation by the Frobenius norm plus eps, the bf16 cast, the rule that
+    a matrix with more rows than columns is iterated as its transpose, the
+    three products per step, and the output dtype (the input's);
+  * the summary paragraph that follows says momentum is Nesterov's and that
+    orthogonalisation comes after it, and that the iteration runs in bfloat16.
+
+Arithmetic contract (the readings are listed in DESIGN.md, "Readings"):
+  * every sum and product is carried in float64 (exact for the bf16 x bf16
+    products, ~1e-16 relative for the sums);
+  * a value is rounded straight from float64 to bfloat16 (round to nearest,
+    ties to even; no detour through float32) at exactly the points where the
+    GPU stores bf16: the scaled input X0, and A, B and X of every step;
+  * momentum rounds each of its two results once to float32.
+
+The one deliberate library primitive is ``numpy.matmul`` in float64, used as
+the plain definition of a matrix product (sum over the shared index).
+"""
+
+import numpy as np
+
+#: Coefficients of the quintic p(x) = a*x + b*x**3 + c*x**5, as printed in the
+#: Muon section's listing.  The GPU uses their float32 values; so does the
+#: oracle (promoted exactly to float64).
+NS5_COEFFS = (3.4445, -4.7750, 2.0315)
+NS5_STEPS = 5
+NS5_EPS = 1e-7
+
+_BF16_MAX = float.fromhex("0x1.fep127")   # largest finite bfloat16, (2 - 2**-7) * 2**127
+_BF16_MIN_QUANTUM_EXP = -133                 # spacing of bf16 subnormals is 2**-133
+
+
+def f32(x):
+    """The float32 value of ``x``, as a Python float (exact float64)."""
+    return float(np.float32(x))
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 has float32's exponent range and an 8-bit significand (7 stored
+    bits plus the implicit one), so a finite value x = m * 2**e with
+    0.5 <= |m| < 1 is rounded to a multiple of 2**(e - 8), or of 2**-133 in the
+    subnormal range.  Scaling by a power of two is exact, so ``rint`` (which
+    rounds half to even) performs the single rounding.  Values whose rounded
+    magnitude exceeds the largest finite bf16 become +-inf.  The result is
+    returned as float64 holding bf16-representable values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, _BF16_MIN_QUANTUM_EXP)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+        r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, x), r)
+        r = np.where(np.isfinite(x), r, x)
+    return r
+
+
+def momentum_nesterov(g, buf, mu=0.95):
+    """One Nesterov-momentum step on a gradient, as the Muon section uses it
+    (summary paragraph: "Nesterov momentum in the update, orthogonalise after
+    momentum").  The update formula itself did not survive in the page; the
+    reading used is plain SGD-Nesterov without dampening:
+
+        buf <- mu * buf + g
+        u   <- g + mu * buf          (with the new buf)
+
+    Each result is formed in float64 from float32 operands and rounded once to
+    float32.  Returns ``(buf_new, u)`` as float32 arrays; inputs are untouched.
+    """
+    mu64 = f32(mu)
+    g64 = np.asarray(g, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(buf, dtype=np.float32).astype(np.float64)
+    buf_new = (mu64 * b64 + g64).astype(np.float32)
+    u = (g64 + mu64 * buf_new.astype(np.float64)).astype(np.float32)
+    return buf_new, u
+
+
+def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):
+    """Quintic Newton-Schulz orthogonalisation of one 2-D matrix, following the
+    Muon section's ``zeroth_power_via_newtonschulz5`` step by step:
+
+        X = bf16(G) / (||G||_F + eps)              rounded to bf16
+        if rows > cols: X = X^T                     (iterate on the short side)
+        repeat ``steps`` times:
+            A = X X^T                               rounded to bf16
+            B = b A + c A A                         rounded to bf16
+            X = a X + B X                           rounded to bf16
+        if rows > cols: X = X^T
+        return X in G's dtype
+
+    The Frobenius norm is taken of the float32 input in float64 and is never
+    rounded to bf16.  Returns a float32 array of G's shape.
+    """
+    G = np.asarray(G)
+    if G.ndim != 2:
+        raise ValueError("ns5 expects a 2-D matrix")
+    a, b, c = (f32(v) for v in coeffs)
+    eps = f32(eps)
+    u = G.astype(np.float32).astype(np.float64)
+    norm = np.sqrt(np.sum(u * u))
+    X = round_bf16(round_bf16(u) / (norm + eps))
+    tall = G.shape[0] > G.shape[1]
+    if tall:
+        X = X.T
+    for _ in range(steps):
+        A = round_bf16(X @ X.T)
+        B = round_bf16(b * A + c * (A @ A))
+        X = round_bf16(a * X + B @ X)
+    if tall:
+        X = X.T
+    return np.ascontiguousarray(X).astype(np.float32)
+
+
+def ns5_grouped(Gs, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):
+    """NS5 of each matrix in a list; the matrices are independent."""
+    return [ns5(G, steps=steps, eps=eps, coeffs=coeffs) for G in Gs]
+
+
+def muon_step(gs, bufs, mu=0.95, steps=NS5_STEPS, eps=NS5_EPS):
+    """Momentum then NS5 for a list of gradient matrices (the order the Muon
+    section's summary paragraph prescribes).  Returns ``(new_bufs, updates)``."""
+    new_bufs, outs = [], []
+    for g, buf in zip(gs, bufs):
+        b, u = momentum_nesterov(g, buf, mu)
+        new_bufs.append(b)
+        outs.append(ns5(u, steps=steps, eps=eps))
+    return new_bufs, outs
+
+
+def ns5_nominal_flops(rows, cols, steps=NS5_STEPS):
+    """Nominal NS5 flop count, 2 flops per multiply-add: per step the products
+    X X^T (2 m^2 n), A A (2 m^3) and B X (2 m^2 n), with m <= n."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (4 * m * m * n + 2 * m ** 3)
