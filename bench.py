@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the Muon hot path on one MI355X.
+
+A step is one whole Muon hot-path pass over the GPT-2 124M hidden-matrix set
+(12 layers x 768x2304, 768x768, 768x3072, 3072x768; synthetic rank-16 plus
+noise gradients and N(0, 0.1^2) momentum buffers, seed 1): Nesterov momentum
+over all 48 gradients (one launch over flat buffers), then NS5 of every
+momentum output, grouped by shape (4 grouped calls).  Inputs are resident in
+HBM before the timed region.
+
+Printed (one JSON line on stdout):
+  value          nominal NS5 flops of the step, sum of 5 (4 m^2 n + 2 m^3),
+                 divided by the measured step time (momentum included), TFLOP/s
+  ms_per_step    the step time
+  roofline       the dominant kernel (the a X + B X product of NS5 steps 1-4)
+                 timed with HIP events around each of its launches, against
+                 the bf16 dense MFMA peak
+  momentum       the momentum kernel alone (16 bytes per element) against HBM
+  ns5_4096       NS5 of one 4096x4096 matrix (U diag(s) V^T, seed 3)
+  cpu_baseline   the CPU oracle on a bounded sample of the same step
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NS5 TFLOP/s (bf16) & % MFMA peak; ms per GPT-2-124M-shaped Muon step"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--skip-cpu-baseline", action="store_true")
+    p.add_argument("--skip-square", action="store_true", help="skip the 4096x4096 NS5 line")
+    p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
+    return p.parse_args()
+
+
+def time_step(st, steps, torch):
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        st.step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def time_dominant_kernel(st, steps, torch, muon):
+    """Second timed pass: the same steps, with HIP events recorded by the
+    library around every a X + B X launch of NS5 steps 1-4."""
+    groups = list(st.groups.items())
+    pairs_per_call = st.steps - 1
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * pairs_per_call)] for _ in groups]
+              for _ in range(steps)]
+    for per_step in events:                     # create the underlying HIP events
+        for evs in per_step:
+            for e in evs:
+                e.record()
+    torch.cuda.synchronize()
+    flops_per_call, recorded = [], []
+    for s in range(steps):
+        st.momentum()
+        for gi, ((r, c), ix) in enumerate(groups):
+            muon.ns5_grouped([st.us[i] for i in ix], [st.outs[i] for i in ix], steps=st.steps, eps=st.eps,
+                             workspace=st.workspace, events=events[s][gi])
+            recorded.append(muon.ns5_grouped.last_recorded)
+            if s == 0:
+                m, n = min(r, c), max(r, c)
+                flops_per_call.append(len(ix) * 2.0 * m * m * n)
+    torch.cuda.synchronize()
+    total_ms, total_flops, launches = 0.0, 0.0, 0
+    k = 0
+    for s in range(steps):
+        for gi in range(len(groups)):
+            evs = events[s][gi]
+            for p in range(recorded[k]):
+                total_ms += evs[2 * p].elapsed_time(evs[2 * p + 1])
+                total_flops += flops_per_call[gi]
+                launches += 1
+            k += 1
+    avg_ms = total_ms / launches
+    achieved = total_flops / (total_ms * 1e-3) / 1e12
+    return {
+        "bound": "mfma",
+        "kernel": "k_gemm_nt<256, GEMM_BX>: X' = a X + B X (NS5 steps 1-4)",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "launches": launches,
+        "avg_launch_us": round(avg_ms * 1e3, 2),
+        "flops_per_launch": total_flops / launches,
+    }
+
+
+def time_momentum(st, steps, torch):
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.momentum()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        st.momentum()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    gbs = st.momentum_bytes() / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "bytes": st.momentum_bytes()}
+
+
+def time_square(torch, muon, workloads, reps=10):
+    G, _, _, _ = workloads.square_4096()
+    g = torch.from_numpy(G).cuda()
+    out = torch.empty_like(g)
+    for _ in range(3):
+        muon.ns5(g, out)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        muon.ns5(g, out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    tf = muon.ns5_flops(4096, 4096) / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
+def cpu_baseline(items):
+    """The oracle, as it stands, on layer 0's four matrices (one of each
+    shape): momentum then NS5, timed on this host's cores."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    sample = [it for it in items if it[0] == 0]
+    flops = sum(oracle.ns5_nominal_flops(*it[2].shape) for it in sample)
+    t0 = time.perf_counter()
+    for _, _, G, buf in sample:
+        _, u = oracle.momentum_nesterov(G, buf, 0.95)
+        oracle.ns5(u)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    del np
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "layer 0 of the GPT-2 124M set (768x2304, 768x768, 768x3072, 3072x768): momentum + NS5, "
+                      f"{flops:.3g} nominal NS5 flops in {dt:.1f} s (float64 BLAS matmuls, single-threaded "
+                      "bf16 rounding)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the Muon hot path here has no multi-GPU path "
+              "(see the sharding design); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from newton_schulz_09_amd import muon, step, workloads
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    items = workloads.gpt2_124m()
+    st = step.MuonStep([it[2].shape for it in items], device="cuda:0")
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s: {len(items)} matrices, {st.total} floats per buffer")
+
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    ms = time_step(st, args.steps, torch)
+    flops = st.nominal_ns5_flops()
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"step: {ms:.4f} ms, {value:.1f} TFLOP/s nominal NS5")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gpt2_124m_hidden_set",
+            "matrices": len(items),
+            "layers": 12,
+            "shapes": ["768x2304", "768x768", "768x3072", "3072x768"],
+            "mu": 0.95,
+            "ns5_steps": 5,
+            "eps": 1e-7,
+            "nominal_ns5_flops": flops,
+        },
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+    }
+    if not args.skip_extras:
+        res["roofline"] = time_dominant_kernel(st, args.steps, torch, muon)
+        log(f"dominant kernel: {res['roofline']}")
+        res["momentum"] = time_momentum(st, args.steps, torch)
+        log(f"momentum: {res['momentum']}")
+        if not args.skip_square:
+            res["ns5_4096"] = time_square(torch, muon, workloads)
+            log(f"ns5 4096: {res['ns5_4096']}")
+        if not args.skip_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(items)
+            log(f"cpu baseline: {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

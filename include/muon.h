@@ -1,0 +1,153 @@
+/*
+ * muon.h - C ABI of libmuon.so, the MI355X (gfx950) hot path of the Muon
+ * optimizer: Nesterov momentum followed by quintic Newton-Schulz
+ * orthogonalisation (NS5) iterated in bfloat16.
+ *
+ * Source of the method: Synced (机器之心) report on Modded-NanoGPT, section
+ * "Muon optimizer" - the printed function zeroth_power_via_newtonschulz5 and
+ * the summary paragraph that follows it (Nesterov momentum, orthogonalise
+ * after momentum, run the iteration in bfloat16).
+ *
+ * Conventions for every entry point
+ *  - Matrices are dense, row-major and contiguous (leading dimension = cols),
+ *    in device memory.  The caller owns every buffer, including the
+ *    workspace; the library allocates nothing and keeps no state between
+ *    calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it and the call returns without synchronising.
+ *  - Arguments are validated before anything is enqueued; a validation error
+ *    returns a non-zero status and enqueues nothing.  A HIP launch error is
+ *    reported as MUON_ERR_HIP; faults during execution surface at the
+ *    caller's next synchronisation.
+ *  - muon_last_error() returns a per-thread message describing the most
+ *    recent non-zero status.
+ *  - Calls that share a workspace must not overlap in time (enqueue them on
+ *    one stream, or give each stream its own workspace).
+ *  - NaN and Inf inputs are not checked; they propagate to the outputs.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad count  */
+    MUON_ERR_UNSUPPORTED = 2,  /* a size beyond the documented limits         */
+    MUON_ERR_WORKSPACE = 3,    /* workspace null or smaller than required     */
+    MUON_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed  */
+} muon_status;
+
+/* Quintic coefficients of p(x) = a x + b x^3 + c x^5 (the printed listing);
+ * the kernels use their float32 values. */
+#define MUON_NS5_A 3.4445f
+#define MUON_NS5_B (-4.7750f)
+#define MUON_NS5_C 2.0315f
+#define MUON_NS5_DEFAULT_STEPS 5
+#define MUON_NS5_DEFAULT_EPS 1e-7f
+
+/* Largest number of matrices one grouped call processes in a single pass;
+ * larger groups are processed in passes of this many, reusing the
+ * workspace. */
+#define MUON_NS5_MAX_GROUP 128
+/* Largest supported min(rows, cols) and max(rows, cols). */
+#define MUON_NS5_MAX_SHORT 16384
+#define MUON_NS5_MAX_LONG (1 << 20)
+
+/*
+ * Nesterov momentum, one step (summary paragraph of the Muon section:
+ * Nesterov momentum in the update; its formula did not survive in the page,
+ * and the plain SGD-Nesterov form without dampening is used):
+ *     buf[i] <- mu * buf[i] + g[i]
+ *     u[i]   <- g[i] + mu * buf[i]          (new buf)
+ * each computed as one float32 fused multiply-add (one rounding).
+ *  g    : [numel] float32, read.
+ *  buf  : [numel] float32, read and overwritten in place (the optimizer state).
+ *  u    : [numel] float32, written; may alias g (in-place update of the
+ *         gradient), must not alias buf.
+ *  numel: >= 0; 0 enqueues nothing and returns MUON_OK.
+ * Errors: MUON_ERR_INVALID_ARG for a null pointer with numel > 0 or
+ * numel < 0, or u == buf.
+ */
+int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, float mu,
+                           void* stream);
+
+/*
+ * Bytes of workspace muon_ns5 / muon_ns5_grouped need for `count` matrices of
+ * rows x cols (count is capped at MUON_NS5_MAX_GROUP, since larger groups
+ * reuse one pass's workspace).  Returns 0 for invalid sizes.  The workspace
+ * must be device memory aligned to 256 bytes; its contents on entry do not
+ * matter.
+ */
+size_t muon_ns5_workspace_size(int64_t rows, int64_t cols, int64_t count);
+
+/*
+ * NS5 of one matrix (the printed zeroth_power_via_newtonschulz5):
+ *     X = bf16( bf16(G) / (||G||_F + eps) )         norm of the fp32 input
+ *     if rows > cols: X = X^T                        iterate on the short side
+ *     repeat `steps` times:
+ *         A = bf16( X X^T )                          bf16 MFMA, fp32 accumulate
+ *         B = bf16( b A + c A A )
+ *         X = bf16( a X + B X )
+ *     out = float32( rows > cols ? X^T : X )
+ * with (a, b, c) = (MUON_NS5_A, MUON_NS5_B, MUON_NS5_C).
+ *  G    : [rows x cols] float32, read only.
+ *  out  : [rows x cols] float32, written (every value is bf16-representable);
+ *         may alias G.
+ *  rows, cols : >= 1, min <= MUON_NS5_MAX_SHORT, max <= MUON_NS5_MAX_LONG.
+ *  steps: >= 0 (0 returns the normalised, bf16-rounded input).
+ *  eps  : > 0 is typical; any finite value is accepted.
+ *  workspace, workspace_bytes: >= muon_ns5_workspace_size(rows, cols, 1).
+ * Errors: MUON_ERR_INVALID_ARG (null pointer, rows/cols < 1, steps < 0,
+ * eps not finite), MUON_ERR_UNSUPPORTED (sizes beyond the limits),
+ * MUON_ERR_WORKSPACE (workspace null, misaligned or too small).
+ */
+int muon_ns5(const float* G, float* out, int64_t rows, int64_t cols, int steps, float eps,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * NS5 of `count` independent matrices of the same shape, batched so that each
+ * kernel launch covers every matrix of a pass (up to MUON_NS5_MAX_GROUP).
+ *  G, out : host arrays of `count` device pointers; out[i] may alias G[i];
+ *           distinct i must not overlap.
+ *  count  : >= 1.
+ *  Everything else as in muon_ns5, with workspace_bytes >=
+ *  muon_ns5_workspace_size(rows, cols, count).
+ * Errors: as muon_ns5, plus MUON_ERR_INVALID_ARG for count < 1 or a null
+ * entry in G or out.
+ */
+int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows,
+                     int64_t cols, int steps, float eps, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Measurement support: exactly muon_ns5_grouped, and in addition records
+ * caller-created hipEvent_t pairs on `stream` around launches of the
+ * a X + B X product of the non-final steps (the dominant kernel of the
+ * iteration): events[2*i] just before and events[2*i+1] just after the i-th
+ * such launch, for i < n_event_pairs.  *recorded (if non-null) receives the
+ * number of pairs recorded.  With events == NULL it is muon_ns5_grouped.
+ * Errors: as muon_ns5_grouped, plus MUON_ERR_INVALID_ARG for
+ * n_event_pairs < 0 or events == NULL with n_event_pairs > 0.
+ */
+int muon_ns5_grouped_timed(const float* const* G, float* const* out, int64_t count, int64_t rows,
+                           int64_t cols, int steps, float eps, void* workspace,
+                           size_t workspace_bytes, void* stream, void* const* events,
+                           int n_event_pairs, int* recorded);
+
+/* Static description of a status code ("ok", "invalid argument", ...). */
+const char* muon_status_string(int status);
+
+/* Per-thread description of the most recent failing call ("" if none). */
+const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

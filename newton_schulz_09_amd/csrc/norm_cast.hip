@@ -1,0 +1,154 @@
+// Frobenius norm and bf16 cast of the NS5 input (the printed
+// zeroth_power_via_newtonschulz5 of the Muon section, Synced report on
+// Modded-NanoGPT: X = G.bfloat16() / (G.norm() + eps), transposed when G has
+// more rows than columns).
+//
+// Two passes, both HBM-bound:
+//   k_sumsq      reads G once (4 B/elem) and writes one float64 partial sum
+//                of squares per workgroup: per-lane float64 accumulation,
+//                wavefront butterfly shuffles, then LDS across the 4 waves.
+//                The split of G into workgroups is fixed, so the result is
+//                deterministic (no atomics).
+//   k_scale_cast reduces a matrix's partials in a fixed order (every
+//                workgroup gets the same float64 norm), then reads G again and
+//                writes X0 = bf16( bf16(G) / (||G|| + eps) ) twice: in G's own
+//                orientation and transposed through an LDS tile (6 B/elem
+//                with 4 B read).  The quotient is formed in float64 and
+//                rounded once to bf16.  Padding to the GEMM tile is written
+//                as zeros.
+#include "internal.hpp"
+
+namespace muon {
+
+namespace {
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_sumsq(ConstPtrTable G, int64_t numel, int nb,
+                                                    int64_t chunk, double* partials) {
+    const int mat = blockIdx.y;
+    const float* g = G.p[mat];
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t end = begin + chunk < numel ? begin + chunk : numel;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int64_t i = begin + threadIdx.x;
+    for (; i + 3 * kThreads < end; i += 4 * kThreads) {
+        const float x0 = g[i], x1 = g[i + kThreads], x2 = g[i + 2 * kThreads], x3 = g[i + 3 * kThreads];
+        s0 = fma(static_cast<double>(x0), static_cast<double>(x0), s0);
+        s1 = fma(static_cast<double>(x1), static_cast<double>(x1), s1);
+        s2 = fma(static_cast<double>(x2), static_cast<double>(x2), s2);
+        s3 = fma(static_cast<double>(x3), static_cast<double>(x3), s3);
+    }
+    for (; i < end; i += kThreads) {
+        const float x = g[i];
+        s0 = fma(static_cast<double>(x), static_cast<double>(x), s0);
+    }
+    double s = wave_sum((s0 + s1) + (s2 + s3));
+    __shared__ double red[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        partials[static_cast<int64_t>(mat) * nb + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+}
+
+constexpr int kCastTile = 64;
+
+__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int rows, int cols, int rows_pad,
+                                                         int cols_pad, int tiles_c, const double* partials,
+                                                         int nb, float eps, bf16_t* nat, int64_t nat_mat,
+                                                         bf16_t* tr, int64_t tr_mat) {
+    const int mat = blockIdx.y;
+    const int tr_i = blockIdx.x / tiles_c, tc_i = blockIdx.x % tiles_c;
+    const int r0 = tr_i * kCastTile, c0 = tc_i * kCastTile;
+    const float* g = G.p[mat];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    __shared__ double s_norm;
+    __shared__ bf16_t tile[kCastTile][kCastTile + 2];
+
+    if (wave == 0) {
+        const double* part = partials + static_cast<int64_t>(mat) * nb;
+        double s = 0.0;
+        for (int k = lane; k < nb; k += 64) s += part[k];
+        s = wave_sum(s);
+        if (lane == 0) s_norm = sqrt(s) + static_cast<double>(eps);
+    }
+    __syncthreads();
+    const double d = s_norm;
+
+    bf16_t* natm = nat + static_cast<int64_t>(mat) * nat_mat;
+    bf16_t* trm = tr + static_cast<int64_t>(mat) * tr_mat;
+
+    // G's orientation: lanes run along the columns (coalesced reads/writes)
+    const int c = lane;
+    for (int r = wave; r < kCastTile; r += kThreads / 64) {
+        const int gr = r0 + r, gc = c0 + c;
+        float v = 0.0f;
+        if (gr < rows && gc < cols) v = g[static_cast<int64_t>(gr) * cols + gc];
+        const double q = static_cast<double>(bf16_to_f32(f32_to_bf16(v))) / d;
+        const bf16_t h = (gr < rows && gc < cols) ? f64_to_bf16(q) : static_cast<bf16_t>(0);
+        natm[static_cast<int64_t>(gr) * cols_pad + gc] = h;
+        tile[r][c] = h;
+    }
+    __syncthreads();
+    // transposed: lanes run along G's rows, which are the columns of tr
+    const int r = lane;
+    for (int cc = wave; cc < kCastTile; cc += kThreads / 64) {
+        trm[static_cast<int64_t>(c0 + cc) * rows_pad + r0 + r] = tile[r][cc];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int cols_pad,
+                                                       const bf16_t* nat, int64_t nat_mat) {
+    const int mat = blockIdx.y;
+    const int64_t total = static_cast<int64_t>(rows) * cols;
+    const bf16_t* src = nat + static_cast<int64_t>(mat) * nat_mat;
+    float* dst = out.p[mat];
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t r = i / cols, c = i - r * cols;
+        dst[i] = bf16_to_f32(src[r * cols_pad + c]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, double* partials,
+                        hipStream_t stream) {
+    const int64_t chunk = (numel + nb - 1) / nb;
+    k_sumsq<<<dim3(nb, cnt), kThreads, 0, stream>>>(G, numel, nb, chunk, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& plan, const double* partials,
+                             float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream) {
+    // G's orientation: rows x cols padded; X is that orientation unless G is tall
+    const int rows_pad = plan.tall ? plan.np : plan.mp;
+    const int cols_pad = plan.tall ? plan.mp : plan.np;
+    const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
+    const int64_t mat_elems = static_cast<int64_t>(plan.x_elems);
+    k_scale_cast<<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
+        G, static_cast<int>(plan.rows), static_cast<int>(plan.cols), rows_pad, cols_pad, tiles_c, partials,
+        plan.nb, eps, nat, mat_elems, tr, mat_elems);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
+                           hipStream_t stream) {
+    const int cols_pad = plan.tall ? plan.mp : plan.np;
+    const int64_t total = plan.rows * plan.cols;
+    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 2048) blocks = 2048;
+    k_copy_out<<<dim3(static_cast<unsigned>(blocks), cnt), kThreads, 0, stream>>>(
+        out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), cols_pad, nat,
+        static_cast<int64_t>(plan.x_elems));
+    return hipGetLastError();
+}
+
+}  // namespace muon

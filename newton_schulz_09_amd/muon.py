@@ -1,0 +1,198 @@
+"""Python binding of libmuon.so (C ABI in include/muon.h).
+
+Argument marshalling only: every step of momentum and NS5 runs in the HIP
+kernels of the library.  PyTorch supplies device memory (the tensors and a
+cached workspace) and the current HIP stream.  Importing this module raises
+if the library has not been built (``python -m newton_schulz_09_amd.build``);
+there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon.so")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = 1
+MUON_ERR_UNSUPPORTED = 2
+MUON_ERR_WORKSPACE = 3
+MUON_ERR_HIP = 4
+
+NS5_STEPS = 5
+NS5_EPS = 1e-7
+MAX_GROUP = 128
+
+#: Every symbol include/muon.h declares.
+EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
+           "muon_ns5_grouped_timed", "muon_status_string", "muon_last_error")
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m newton_schulz_09_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.muon_momentum_nesterov.argtypes = [vp, vp, vp, i64, ctypes.c_float, vp]
+    lib.muon_momentum_nesterov.restype = ctypes.c_int
+    lib.muon_ns5_workspace_size.argtypes = [i64, i64, i64]
+    lib.muon_ns5_workspace_size.restype = sz
+    lib.muon_ns5.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    lib.muon_ns5.restype = ctypes.c_int
+    lib.muon_ns5_grouped.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_float, vp, sz, vp]
+    lib.muon_ns5_grouped.restype = ctypes.c_int
+    lib.muon_ns5_grouped_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
+                                           ctypes.c_float, vp, sz, vp, ctypes.POINTER(vp), ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_int)]
+    lib.muon_ns5_grouped_timed.restype = ctypes.c_int
+    lib.muon_status_string.argtypes = [ctypes.c_int]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_last_error.argtypes = []
+    lib.muon_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != MUON_OK:
+        msg = lib.muon_status_string(status).decode()
+        detail = lib.muon_last_error().decode()
+        raise MuonError(status, f"{msg}: {detail}" if detail else msg)
+
+
+def _stream_handle(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_f32_cuda(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def momentum_nesterov(g, buf, u=None, mu=0.95):
+    """buf <- mu*buf + g ; u <- g + mu*buf (new buf), in one kernel.
+    ``u`` may be ``g`` (in-place); returns ``u``."""
+    _require_f32_cuda(g, "g")
+    _require_f32_cuda(buf, "buf")
+    if buf.numel() != g.numel() or buf.device != g.device:
+        raise ValueError("g and buf must have the same size and device")
+    if u is None:
+        u = torch.empty_like(g)
+    _require_f32_cuda(u, "u")
+    if u.numel() != g.numel() or u.device != g.device:
+        raise ValueError("u must have the size and device of g")
+    _check(lib.muon_momentum_nesterov(g.data_ptr(), buf.data_ptr(), u.data_ptr(), g.numel(), float(mu),
+                                      _stream_handle(g.device)))
+    return u
+
+
+def workspace_size(rows, cols, count=1):
+    return int(lib.muon_ns5_workspace_size(rows, cols, count))
+
+
+_workspaces = {}
+
+
+def _workspace(device, stream, nbytes):
+    """A cached uint8 device buffer per (device, stream), grown on demand.
+    Calls on one stream are ordered, so they can share it."""
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def ns5(G, out=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
+    """Quintic Newton-Schulz orthogonalisation of one 2-D float32 matrix.
+    Returns ``out`` (a new tensor unless given; may be ``G``)."""
+    _require_f32_cuda(G, "G")
+    if G.dim() != 2:
+        raise ValueError("G must be 2-D")
+    rows, cols = G.shape
+    if out is None:
+        out = torch.empty_like(G)
+    _require_f32_cuda(out, "out")
+    if out.shape != G.shape or out.device != G.device:
+        raise ValueError("out must have G's shape and device")
+    need = workspace_size(rows, cols, 1)
+    if need == 0:
+        raise MuonError(MUON_ERR_UNSUPPORTED, f"shape {rows}x{cols} is not supported")
+    stream = _stream_handle(G.device)
+    ws = workspace if workspace is not None else _workspace(G.device, stream, need)
+    _check(lib.muon_ns5(G.data_ptr(), out.data_ptr(), rows, cols, int(steps), float(eps), ws.data_ptr(),
+                        ws.numel() * ws.element_size(), stream))
+    return out
+
+
+def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None):
+    """NS5 of a list of same-shaped float32 matrices, batched per launch.
+    Returns the list of outputs (new tensors unless given).
+
+    ``events`` (measurement): a list of ``torch.cuda.Event(enable_timing=True)``
+    pairs ``[start0, stop0, start1, stop1, ...]``; the library records them
+    around the a X + B X launches of the non-final steps.  The number of
+    pairs recorded is then available as ``ns5_grouped.last_recorded``."""
+    Gs = list(Gs)
+    if not Gs:
+        return []
+    for i, G in enumerate(Gs):
+        _require_f32_cuda(G, f"Gs[{i}]")
+    shape, device = Gs[0].shape, Gs[0].device
+    if len(shape) != 2 or any(G.shape != shape or G.device != device for G in Gs):
+        raise ValueError("all matrices must be 2-D with the same shape and device")
+    if outs is None:
+        outs = [torch.empty_like(G) for G in Gs]
+    outs = list(outs)
+    if len(outs) != len(Gs):
+        raise ValueError("outs must match Gs in length")
+    for i, o in enumerate(outs):
+        _require_f32_cuda(o, f"outs[{i}]")
+        if o.shape != shape or o.device != device:
+            raise ValueError("every output must have the inputs' shape and device")
+    rows, cols = shape
+    count = len(Gs)
+    need = workspace_size(rows, cols, count)
+    if need == 0:
+        raise MuonError(MUON_ERR_UNSUPPORTED, f"shape {rows}x{cols} is not supported")
+    stream = _stream_handle(device)
+    ws = workspace if workspace is not None else _workspace(device, stream, need)
+    g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
+    o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    if events is None:
+        _check(lib.muon_ns5_grouped(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps), ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), stream))
+    else:
+        if len(events) % 2:
+            raise ValueError("events must come in (start, stop) pairs")
+        ev = (ctypes.c_void_p * max(len(events), 1))(*[e.cuda_event for e in events])
+        rec = ctypes.c_int(0)
+        _check(lib.muon_ns5_grouped_timed(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps),
+                                          ws.data_ptr(), ws.numel() * ws.element_size(), stream, ev,
+                                          len(events) // 2, ctypes.byref(rec)))
+        ns5_grouped.last_recorded = rec.value
+    return outs
+
+
+def ns5_flops(rows, cols, steps=NS5_STEPS):
+    """Nominal NS5 flop count (2 per multiply-add): steps * (4 m^2 n + 2 m^3),
+    m = min(rows, cols), n = max(rows, cols)."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (4 * m * m * n + 2 * m ** 3)

@@ -2,8 +2,10 @@
 
 This module holds input generation and nothing of the method's arithmetic:
 it is the one piece that both the GPU tests and the CPU oracle are fed from.
-Every draw uses ``numpy.random.default_rng(seed)`` (PCG64) in the order
-documented per workload, so a workload is fully defined by its seed.
+Every draw uses ``numpy.random.default_rng`` (PCG64).  Where a workload has
+many matrices, each matrix has its own generator seeded with the tuple
+(seed, layer, shape index) or (seed, index), so any subset can be generated
+on its own and the workload is fully defined by its seed.
 
 Workloads (shapes are rows x cols of the fp32 gradient G):
 
@@ -11,7 +13,8 @@ Workloads (shapes are rows x cols of the fp32 gradient G):
   float32; the momentum buffer starts at zero; its 128x64 transpose exercises
   the tall path.
 * ``gpt2_124m``       - seed 1.  12 layers x (768x2304, 768x768, 768x3072,
-  3072x768), the hidden matrices of GPT-2 124M.  Per matrix, in this order:
+  3072x768), the hidden matrices of GPT-2 124M.  Per matrix, from
+  default_rng((seed, layer, shape_index)), in this order:
   L (m x 16), R (16 x n), N (m x n) ~ N(0,1) and a momentum buffer
   0.1 * N(0,1), all drawn as float32; G = L R / 4 + 0.1 N in float32 (a rank-16
   signal plus noise, standing in for a training gradient).
@@ -19,9 +22,11 @@ Workloads (shapes are rows x cols of the fp32 gradient G):
   QR of 4096x4096 N(0,1) matrices (float64), s log-uniform on [1e-3, 1].
 * ``gpt2_1p5b``       - seed 4.  As ``gpt2_124m`` with 48 layers x (1600x4800,
   1600x1600, 1600x6400, 6400x1600), the hidden matrices of GPT-2 1.5B.
+  Per matrix generator: default_rng((seed, layer, shape_index)).
 * ``extreme_aspect``  - seed 5.  Eight 2048x8192 then eight 8192x2048 matrices
   G = U diag(s) V^T with U, V from reduced QR of float32 N(0,1) draws,
-  s log-uniform on [1e-4, 1] and a random quarter of s set to exactly 0.
+  s log-uniform on [1e-4, 1] and a random quarter of s set to exactly 0;
+  matrix i (0..15) draws from default_rng((seed, i)).
 """
 
 import numpy as np
@@ -52,28 +57,18 @@ def _lowrank_plus_noise(rng, rows, cols, rank=16):
 def gpt_hidden_set(shapes, layers, seed, only_shape=None):
     """Gradients and momentum buffers for ``layers`` x ``shapes``.
 
-    Returns a list of ``(layer, shape_index, G, buf)``.  All draws are made in
-    the documented order; ``only_shape`` (a shape index) keeps just that class
-    in the result without changing any draw.
+    Returns a list of ``(layer, shape_index, G, buf)``, layer-major.
+    ``only_shape`` (a shape index) generates just that class.
     """
-    rng = np.random.default_rng(seed)
     out = []
     for layer in range(layers):
         for si, (r, c) in enumerate(shapes):
             if only_shape is not None and si != only_shape:
-                # advance the generator exactly as a full draw would
-                _skip_lowrank_plus_noise(rng, r, c)
                 continue
+            rng = np.random.default_rng((seed, layer, si))
             G, buf = _lowrank_plus_noise(rng, r, c)
             out.append((layer, si, G, buf))
     return out
-
-
-def _skip_lowrank_plus_noise(rng, rows, cols, rank=16):
-    rng.standard_normal((rows, rank), dtype=np.float32)
-    rng.standard_normal((rank, cols), dtype=np.float32)
-    rng.standard_normal((rows, cols), dtype=np.float32)
-    rng.standard_normal((rows, cols), dtype=np.float32)
 
 
 def gpt2_124m(seed=1, only_shape=None):
@@ -104,19 +99,21 @@ def extreme_aspect_one(rng, rows, cols):
     return G, U, s, V
 
 
-def extreme_aspect(seed=5, wide=(2048, 8192), count=8, which=None):
-    """Eight wide then eight tall matrices; ``which`` ('wide' or 'tall')
-    returns only that half (the draws for the other half are still made
-    first when 'tall' is asked, so the matrices are the same)."""
-    rng = np.random.default_rng(seed)
+def extreme_aspect(seed=5, wide=(2048, 8192), count=8, which=None, indices=None):
+    """``count`` wide then ``count`` tall matrices as ``(G, U, s, V)``;
+    ``which`` ('wide' or 'tall') keeps one half, ``indices`` (within the half
+    or the whole list) a subset."""
+    idx = list(range(2 * count))
+    if which == "wide":
+        idx = idx[:count]
+    elif which == "tall":
+        idx = idx[count:]
+    if indices is not None:
+        idx = [idx[i] for i in indices]
     out = []
-    for i in range(2 * count):
+    for i in idx:
         shape = wide if i < count else (wide[1], wide[0])
-        item = extreme_aspect_one(rng, *shape)
-        if which is None or (which == "wide") == (i < count):
-            out.append(item)
-        if which == "wide" and i == count - 1:
-            break
+        out.append(extreme_aspect_one(np.random.default_rng((seed, i)), *shape))
     return out
 
 

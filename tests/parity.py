@@ -1,0 +1,75 @@
+"""Comparison helpers for GPU-vs-oracle parity.
+
+Tolerances (stated for the NS5 output of every matrix): relative Frobenius
+error <= 1e-2 against the oracle, and every sorted singular value within 0.02
+of the oracle's.  The oracle accumulates in float64 and the GPU in float32,
+which flips a few bf16 roundings that the iteration then amplifies; the
+measured spread of that effect on these workloads is 5e-4 .. 7e-3, so the
+bound is the accumulation difference with margin, not slack for errors.
+Momentum is float32 arithmetic with one rounding per result: at most 1 ulp
+apart (the oracle rounds float64 -> float32, which can differ from a single
+fused rounding only at a float64-made tie).
+"""
+
+import numpy as np
+import torch
+
+REL_FRO_TOL = 1e-2
+SIGMA_TOL = 0.02
+
+
+def to_np(t):
+    return t.detach().to("cpu").numpy()
+
+
+def rel_fro(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    num = np.linalg.norm(got - want)
+    return num / den if den > 0 else num
+
+
+def svals(M):
+    """Singular values, float64, descending (LAPACK through torch on the CPU)."""
+    t = torch.from_numpy(np.ascontiguousarray(M, dtype=np.float64))
+    return torch.linalg.svdvals(t).numpy()
+
+
+def assert_ns5_parity(got, want, name="", check_sigma=True):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    r = rel_fro(got, want)
+    assert r <= REL_FRO_TOL, f"{name}: relative Frobenius error {r:.3g} > {REL_FRO_TOL}"
+    if check_sigma:
+        d = np.max(np.abs(svals(got) - svals(want)))
+        assert d <= SIGMA_TOL, f"{name}: singular values differ by {d:.3g} > {SIGMA_TOL}"
+    return r
+
+
+def ulp_diff32(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    ia = a.view(np.int32).astype(np.int64)
+    ib = b.view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)
+
+
+def bf16_ulp_diff(a, b):
+    """Distance in bf16 steps between two arrays of bf16-valued float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    ia = (a.view(np.uint32) >> 16).astype(np.int64)
+    ib = (b.view(np.uint32) >> 16).astype(np.int64)
+    ia = np.where(ia >= 0x8000, -(ia & 0x7FFF), ia)
+    ib = np.where(ib >= 0x8000, -(ib & 0x7FFF), ib)
+    return np.abs(ia - ib)
+
+
+def is_bf16_valued(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return bool(np.all((a.view(np.uint32) & 0xFFFF) == 0))

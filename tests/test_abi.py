@@ -1,0 +1,98 @@
+"""The C ABI without a GPU: libmuon.so loads, exports every function that
+include/muon.h declares, sizes workspaces, and rejects invalid arguments
+before it touches the HIP runtime (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def muon():
+    from newton_schulz_09_amd import muon as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(muon_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for need in ("muon_momentum_nesterov", "muon_ns5", "muon_ns5_grouped", "muon_ns5_workspace_size"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(muon):
+    declared = _declared_functions()
+    assert sorted(muon.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(muon.lib, name), name
+
+
+def test_workspace_size(muon):
+    # X, X^T twice each (bf16, padded to the tile) + A, B + norm partials
+    s = muon.workspace_size(64, 128, 1)
+    assert s >= 4 * 64 * 128 * 2 + 2 * 64 * 64 * 2
+    assert muon.workspace_size(128, 64, 1) == s               # orientation-independent
+    assert muon.workspace_size(768, 2304, 12) > 12 * 4 * 768 * 2304 * 2
+    assert muon.workspace_size(768, 2304, 500) == muon.workspace_size(768, 2304, 128)
+    assert muon.workspace_size(0, 5, 1) == 0
+    assert muon.workspace_size(5, 5, 0) == 0
+    assert muon.workspace_size(20000, 20000, 1) == 0           # short side beyond the limit
+    assert muon.workspace_size(1, 1, 1) > 0
+
+
+def test_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    fake = ctypes.c_void_p(0x100000)            # never dereferenced: calls fail validation first
+    ws_small = ctypes.c_void_p(0x200000)
+    # momentum
+    assert lib.muon_momentum_nesterov(None, None, None, 0, 0.95, None) == muon.MUON_OK
+    assert lib.muon_momentum_nesterov(None, fake, fake, 4, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_momentum_nesterov(fake, fake, fake, -1, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_momentum_nesterov(fake, fake, fake, 8, 0.95, None) == muon.MUON_ERR_INVALID_ARG  # u == buf
+    assert b"alias" in lib.muon_last_error()
+    # ns5
+    need = muon.workspace_size(64, 128, 1)
+    assert lib.muon_ns5(None, fake, 64, 128, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 0, 128, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, -1, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, 5, float("nan"), ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, None, need, None) == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, ctypes.c_void_p(0x200010), need, None) \
+        == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, ws_small, need - 1, None) == muon.MUON_ERR_WORKSPACE
+    assert b"needed" in lib.muon_last_error()
+    assert lib.muon_ns5(fake, fake, 1 << 15, 1 << 15, 5, 1e-7, ws_small, 1 << 40, None) \
+        == muon.MUON_ERR_UNSUPPORTED
+    # grouped
+    arr = (ctypes.c_void_p * 2)(0x100000, 0)
+    ok = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    need2 = muon.workspace_size(64, 128, 2)
+    assert lib.muon_ns5_grouped(ok, arr, 2, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(ok, ok, 0, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(None, ok, 2, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(ok, ok, 2, 64, 128, 5, 1e-7, ws_small, need2 - 256, None) \
+        == muon.MUON_ERR_WORKSPACE
+
+
+def test_status_strings(muon):
+    for code in range(5):
+        assert muon.lib.muon_status_string(code)
+    assert muon.lib.muon_status_string(99) == b"unknown status"
+
+
+def test_binding_rejects_cpu_tensors(muon):
+    import torch
+    g = torch.zeros(4)
+    with pytest.raises(ValueError):
+        muon.momentum_nesterov(g, g.clone())
+    with pytest.raises(ValueError):
+        muon.ns5(torch.zeros(4, 4))

@@ -1,0 +1,123 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch
+configuration the benchmark times (flat momentum, grouped NS5 per shape).
+Where the oracle cannot finish every matrix in seconds, it checks sampled
+matrices (each matrix of a group is an independent output) and properties
+that hold at any size check the rest."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from newton_schulz_09_amd import workloads
+
+from . import parity
+
+pytestmark = pytest.mark.gpu
+
+COEFFS = tuple(float(np.float32(v)) for v in oracle.NS5_COEFFS)
+
+
+@pytest.fixture(scope="module")
+def mods():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from newton_schulz_09_amd import muon, step
+    return muon, step
+
+
+def p5(x):
+    for _ in range(5):
+        x = COEFFS[0] * x + COEFFS[1] * x ** 3 + COEFFS[2] * x ** 5
+    return x
+
+
+def _run_step(step_mod, items, shapes):
+    st = step_mod.MuonStep(shapes)
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.timeout(900)
+def test_gpt2_124m_step_all_matrices(mods):
+    """GPT-2 124M hidden-matrix set: one full step, every matrix checked."""
+    _, step_mod = mods
+    items = workloads.gpt2_124m()
+    st = _run_step(step_mod, items, [it[2].shape for it in items])
+    worst = 0.0
+    for k, (layer, si, G, buf) in enumerate(items):
+        want_b, want_u = oracle.momentum_nesterov(G, buf, 0.95)
+        assert parity.ulp_diff32(parity.to_np(st.bufs[k]), want_b).max() <= 1
+        assert parity.ulp_diff32(parity.to_np(st.us[k]), want_u).max() <= 1
+        got = parity.to_np(st.outs[k])
+        r = parity.assert_ns5_parity(got, oracle.ns5(want_u), f"layer {layer} shape {G.shape}")
+        worst = max(worst, r)
+    print(f"gpt2-124m worst relative Frobenius error {worst:.3g}", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_square_4096(mods):
+    """4096x4096 G = U diag(s) V^T: parity with the oracle, and the closed
+    form - the output's singular values are p^5 of s/||G||_F wherever that
+    is well inside the attractor (bf16 noise aside)."""
+    muon, _ = mods
+    G, U, s, V = workloads.square_4096()
+    out = parity.to_np(muon.ns5(torch.from_numpy(G).cuda()))
+    parity.assert_ns5_parity(out, oracle.ns5(G), "4096x4096")
+    # U^T O V is diagonal with p^5(s_i / ||G||_F) in exact arithmetic
+    pred = p5(s / (np.linalg.norm(G.astype(np.float64)) + 1e-7))
+    d = np.diag(U.T @ out.astype(np.float64) @ V)
+    err = np.abs(d - pred)
+    print(f"4096 closed form: max |diag(U^T O V) - p^5| = {err.max():.3g}", flush=True)
+    assert err.max() < 0.02
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("shape_index", [0, 1, 2, 3])
+def test_gpt2_1p5b_group_sampled(mods, shape_index):
+    """GPT-2 1.5B hidden-matrix set, one shape class (48 matrices) per case:
+    momentum and grouped NS5 over the whole class, oracle on the first and the
+    last matrix of the class."""
+    _, step_mod = mods
+    items = workloads.gpt2_1p5b(only_shape=shape_index)
+    st = _run_step(step_mod, items, [it[2].shape for it in items])
+    for k in (0, len(items) - 1):
+        layer, si, G, buf = items[k]
+        want_b, want_u = oracle.momentum_nesterov(G, buf, 0.95)
+        assert parity.ulp_diff32(parity.to_np(st.bufs[k]), want_b).max() <= 1
+        assert parity.ulp_diff32(parity.to_np(st.us[k]), want_u).max() <= 1
+        parity.assert_ns5_parity(parity.to_np(st.outs[k]), oracle.ns5(want_u), f"layer {layer} {G.shape}")
+    # every matrix: finite, bf16-valued, and orthogonal-ish (singular values
+    # of a rank-16-plus-noise update cluster in the attractor band)
+    for k in range(len(items)):
+        o = st.outs[k]
+        assert torch.isfinite(o).all().item()
+    s = parity.svals(parity.to_np(st.outs[len(items) // 2]))
+    assert s.max() < 1.25 and np.median(s) > 0.3
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", ["wide", "tall"])
+def test_extreme_aspect_sampled(mods, which):
+    """Eight 2048x8192 (or 8192x2048, the transpose path) rank-deficient
+    matrices in one grouped call: oracle on two of them; for all eight the
+    zero singular values stay near zero and the others follow p^5."""
+    muon, _ = mods
+    items = workloads.extreme_aspect(which=which)
+    Gs = [torch.from_numpy(it[0]).cuda() for it in items]
+    outs = [parity.to_np(o) for o in muon.ns5_grouped(Gs)]
+    for k in (0, len(items) - 1):
+        parity.assert_ns5_parity(outs[k], oracle.ns5(items[k][0]), f"{which} #{k}")
+    for k, (G, U, s, V) in enumerate(items):
+        pred = p5(s / (np.linalg.norm(G.astype(np.float64)) + 1e-7))
+        d = np.diag(U.T.astype(np.float64) @ outs[k].astype(np.float64) @ V.astype(np.float64))
+        err = np.abs(d - pred)
+        print(f"{which} #{k}: closed form error nonzero {err[s > 0].max():.3g} "
+              f"null {err[s == 0].max():.3g}", flush=True)
+        assert err[s > 0].max() < 0.03, f"{which} #{k}"
+        # rounding noise amplified along the null space stays well below the band
+        assert err[s == 0].max() < 0.2, f"{which} #{k}"
