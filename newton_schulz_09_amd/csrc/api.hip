@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <string>
 
@@ -40,12 +41,32 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 // GEMM tile edge for the short side m.  Padding m and n to the tile keeps the
 // GEMMs free of edge handling; the choice trades padded work against the
-// larger tile's better operand reuse.
+// larger tile's better operand reuse.  MUON_NS5_TILE=64/128/256 in the
+// environment forces one edge for every shape (read once, for tuning sweeps).
 int choose_tile(int64_t m) {
+    static const int forced = [] {
+        const char* s = getenv("MUON_NS5_TILE");
+        const int t = s ? atoi(s) : 0;
+        return (t == 64 || t == 128 || t == 256) ? t : 0;
+    }();
+    if (forced) return forced;
     if (m <= 64) return 64;
-    if (m <= 640) return 128;
-    if (m % 256 == 0 || m >= 2048) return 256;
-    return 128;
+    // 256-wide tiles reuse each operand panel twice as much but give a
+    // quarter of the workgroups: below m = 2048 the 128 tile fills the 256
+    // CUs better (measured on the 768- and 1600-class shapes)
+    if (m < 2048) return 128;
+    return 256;
+}
+
+// Row skew (elements) added to every workspace row stride: 64 bf16 = 128
+// bytes, one cache line (MUON_LD_SKEW=0/32/64/128 overrides it, for tuning).
+int ld_skew() {
+    static const int skew = [] {
+        const char* s = getenv("MUON_LD_SKEW");
+        const int v = s ? atoi(s) : 64;
+        return (v == 0 || v == 32 || v == 64 || v == 128) ? v : 64;
+    }();
+    return skew;
 }
 
 // A dispatch's grid (workgroups x 256 work-items) must fit in 32 bits.
@@ -73,15 +94,20 @@ bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* p) {
     if (cnt * bx_tiles > kMaxWorkgroups) cnt = kMaxWorkgroups / bx_tiles;
     if (cnt < 1) return false;
     p->cnt = static_cast<int>(cnt);
-    p->x_elems = static_cast<size_t>(p->mp) * p->np;
-    p->a_elems = static_cast<size_t>(p->mp) * p->mp;
+    p->ldx = p->np + ld_skew();
+    p->ldxt = p->mp + ld_skew();
+    p->lda = p->mp + ld_skew();
+    p->x_elems = static_cast<size_t>(p->mp) * p->ldx;
+    p->xt_elems = static_cast<size_t>(p->np) * p->ldxt;
+    p->a_elems = static_cast<size_t>(p->mp) * p->lda;
     size_t off = 0;
     const size_t xb = align256(cnt * p->x_elems * sizeof(bf16_t));
+    const size_t xtb = align256(cnt * p->xt_elems * sizeof(bf16_t));
     const size_t ab = align256(cnt * p->a_elems * sizeof(bf16_t));
     p->off_x[0] = off; off += xb;
     p->off_x[1] = off; off += xb;
-    p->off_xt[0] = off; off += xb;
-    p->off_xt[1] = off; off += xb;
+    p->off_xt[0] = off; off += xtb;
+    p->off_xt[1] = off; off += xtb;
     p->off_a = off; off += ab;
     p->off_b = off; off += ab;
     p->off_part = off; off += align256(cnt * p->nb * sizeof(double));
@@ -125,7 +151,8 @@ int run_ns5(const float* const* G, float* const* out, int64_t count, int64_t row
     double* part = reinterpret_cast<double*>(base + plan.off_part);
     const int T = plan.tile;
     const int tiles_m = plan.mp / T, tiles_n = plan.np / T;
-    const int64_t xe = static_cast<int64_t>(plan.x_elems), ae = static_cast<int64_t>(plan.a_elems);
+    const int64_t xe = static_cast<int64_t>(plan.x_elems), xte = static_cast<int64_t>(plan.xt_elems);
+    const int64_t ae = static_cast<int64_t>(plan.a_elems);
 
     for (int64_t start = 0; start < count; start += plan.cnt) {
         const int cnt = static_cast<int>(count - start < plan.cnt ? count - start : plan.cnt);
@@ -152,31 +179,31 @@ int run_ns5(const float* const* G, float* const* out, int64_t count, int64_t row
             const bool last = (s == steps - 1);
             GemmArgs g{};
             // A = X X^T
-            g.P = X[cur]; g.p_mat = xe; g.ldp = plan.np;
-            g.Q = X[cur]; g.q_mat = xe; g.ldq = plan.np;
+            g.P = X[cur]; g.p_mat = xe; g.ldp = plan.ldx;
+            g.Q = X[cur]; g.q_mat = xe; g.ldq = plan.ldx;
             g.kpad = static_cast<int>(round_up(plan.n, 64));
             g.tiles = tiles_m; g.tiles_n = tiles_m; g.tiles_per_mat = tiles_m * (tiles_m + 1) / 2;
-            g.C = A; g.c_mat = ae; g.ldc = plan.mp;
+            g.C = A; g.c_mat = ae; g.ldc = plan.lda;
             e = launch_gemm(GEMM_SYRK, T, g, cnt, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
             // B = b A + c A A
-            g.P = A; g.p_mat = ae; g.ldp = plan.mp;
-            g.Q = A; g.q_mat = ae; g.ldq = plan.mp;
+            g.P = A; g.p_mat = ae; g.ldp = plan.lda;
+            g.Q = A; g.q_mat = ae; g.ldq = plan.lda;
             g.kpad = static_cast<int>(round_up(plan.m, 64));
-            g.C = B; g.c_mat = ae; g.ldc = plan.mp;
-            g.E = A; g.e_mat = ae; g.lde = plan.mp;
+            g.C = B; g.c_mat = ae; g.ldc = plan.lda;
+            g.E = A; g.e_mat = ae; g.lde = plan.lda;
             g.alpha = MUON_NS5_B; g.beta = MUON_NS5_C;
             e = launch_gemm(GEMM_AAB, T, g, cnt, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");
             // X' = a X + B X
-            g.P = B; g.p_mat = ae; g.ldp = plan.mp;
-            g.Q = XT[cur]; g.q_mat = xe; g.ldq = plan.mp;
+            g.P = B; g.p_mat = ae; g.ldp = plan.lda;
+            g.Q = XT[cur]; g.q_mat = xte; g.ldq = plan.ldxt;
             g.kpad = static_cast<int>(round_up(plan.m, 64));
             g.tiles = tiles_m; g.tiles_n = tiles_n; g.tiles_per_mat = tiles_m * tiles_n;
-            g.E = XT[cur]; g.e_mat = xe; g.lde = plan.mp;
+            g.E = XT[cur]; g.e_mat = xte; g.lde = plan.ldxt;
             g.alpha = MUON_NS5_A; g.beta = 1.0f;
-            g.C = X[nxt]; g.c_mat = xe; g.ldc = plan.np;
-            g.CT = XT[nxt]; g.ct_mat = xe; g.ldct = plan.mp;
+            g.C = X[nxt]; g.c_mat = xe; g.ldc = plan.ldx;
+            g.CT = XT[nxt]; g.ct_mat = xte; g.ldct = plan.ldxt;
             g.m = plan.m; g.n = plan.n; g.tall = plan.tall ? 1 : 0;
             const bool timed = sink && !last && sink->recorded < sink->pairs;
             if (timed) {

@@ -10,40 +10,99 @@
 //
 // All three are "NT" products  C[i][j] = sum_k P[i][k] Q[j][k]  with both
 // operands contiguous along k, which is the operand layout of the CDNA
-// matrix cores.  Engine: 256 threads = 4 wavefronts of 64 lanes in a 2x2
-// arrangement, each wave owning a (T/2)x(T/2) sub-tile built from 32x32 MFMA
-// fragments (v_mfma_f32_32x32x16_bf16, fp32 accumulation); K advances 64 at a
-// time through double-buffered LDS tiles (one barrier per K step, the next
-// tile's global loads in flight while the current one is multiplied).  LDS
-// rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with the row so
-// that both the row-wise stores and the fragment loads are bank-conflict
-// free.  Matrices of a group are batched into one launch (blockIdx.x encodes
-// matrix and tile).
+// matrix cores.
+//
+// Engine (gfx950): 256 threads = 4 wavefronts of 64 lanes in a 2x2
+// arrangement, each wave owning a (BM/2)x(BN/2) sub-tile built from 32x32
+// MFMA fragments (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  K advances
+// BK at a time through a ring of STAGES LDS buffers filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each lane supplies a global
+// address, the 64 lanes' 16-byte pieces land contiguously in LDS), so the
+// loads of the next STAGES-1 K steps are in flight while one is multiplied,
+// without passing through registers.  One barrier per K step; the waits are
+// issued explicitly so that only the loads of the step about to be used are
+// waited for.  Inside a K step the MFMAs, the LDS fragment reads and the
+// global->LDS loads are issued interleaved in a fixed order.
+//
+// LDS layout: row-major tiles of BK bf16 per row.  The 16-byte chunk c of
+// row r is stored at slot c ^ f(r); the loads place it there by choosing
+// which global chunk each lane fetches.  f spreads the fragment reads (32
+// consecutive rows, one chunk each, 16 bytes per lane) over all banks whether
+// the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+//
+// Work distribution: one workgroup per output tile, every matrix of a group
+// in the same launch.  Consecutive workgroups are dispatched round-robin over
+// the 8 XCDs (each with its own L2), so the workgroup index is remapped to
+// give every XCD a contiguous range of tiles; within a matrix, tiles of the
+// full grid are ordered in bands of kBand tile rows (column by column inside
+// a band), so that the tiles resident on one XCD share operand panels.
+#include <stdlib.h>
+
 #include "internal.hpp"
 
 namespace muon {
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int kXcds = 8;
+constexpr int kBand = 4;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const void* global_cptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int T, int KIND>
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup b of G -> logical index, so that XCD x (which receives the
+// workgroups b = x, x + 8, ...) processes one contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+    const int q = G / kXcds, r = G % kXcds, x = b % kXcds;
+    return x * q + (x < r ? x : r) + b / kXcds;
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
+    return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+// Slot permutation of row r for CPR 16-byte chunks per row (8 or 4).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CPR == 8) return ((r >> 1) ^ (r << 2)) & 7;
+    else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS operations are done, then barrier.  Written as one
+// asm statement with a memory clobber so the compiler keeps LDS accesses on
+// their side of it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int BK, int STAGES, int KIND>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
-    constexpr int BM = T, BN = T;
+    static_assert(!SYM || BM == BN, "symmetric products use square tiles");
+    static_assert(BK == 64 || BK == 32, "BK is 32 or 64");
+    static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
     constexpr int WTM = BM / 2, WTN = BN / 2;  // wave sub-tile
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int CH_P = BM * (BK / 8) / kThreads;  // 16-byte chunks per thread per operand
-    constexpr int CH_Q = BN * (BK / 8) / kThreads;
-    static_assert(CH_P >= 1 && CH_Q >= 1, "tile too small for the loader");
+    constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row
+    constexpr int RPI = 64 / CPR;          // rows filled by one wave-wide 1 KB load
+    constexpr int IP = BM / RPI / 4;       // loads per wave per stage, P operand
+    constexpr int IQ = BN / RPI / 4;       // and Q operand
+    constexpr int NLOAD = IP + IQ;
+    constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+    static_assert(IP >= 1 && IQ >= 1, "tile too small for the loader");
 
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BM + BN) * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[STAGES * STAGE];
 
     // ---- which matrix and which output tile
-    const int mat = blockIdx.x / args.tiles_per_mat;
-    int t = blockIdx.x - mat * args.tiles_per_mat;
+    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int mat = lid / args.tiles_per_mat;
+    int t = lid - mat * args.tiles_per_mat;
     int ti, tj;
     if constexpr (SYM) {
         ti = 0;
@@ -55,43 +114,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
         }
         tj = ti + t;
     } else {
-        ti = t / args.tiles_n;
-        tj = t - ti * args.tiles_n;
+        const int per_band = kBand * args.tiles_n;
+        const int band = t / per_band;
+        const int first = band * kBand;
+        const int rows_in_band = args.tiles - first < kBand ? args.tiles - first : kBand;
+        const int w = t - band * per_band;
+        ti = first + w % rows_in_band;
+        tj = w / rows_in_band;
     }
     const int i0 = ti * BM, j0 = tj * BN;
-    const bf16_t* P = args.P + mat * args.p_mat + static_cast<int64_t>(i0) * args.ldp;
-    const bf16_t* Q = args.Q + mat * args.q_mat + static_cast<int64_t>(j0) * args.ldq;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    uint4 regP[CH_P], regQ[CH_Q];
-    auto gload = [&](int k0) {
+    // ---- loader: load i of this wave fills rows r0 = (wave*IP + i)*RPI ..
+    // r0 + RPI - 1 of its operand; lane l covers row r0 + l / CPR and LDS slot
+    // l % CPR, so it fetches global chunk (l % CPR) ^ f(row).
+    const bf16_t* gp[IP];
+    const bf16_t* gq[IQ];
+    {
+        const bf16_t* P = args.P + mat * args.p_mat + static_cast<int64_t>(i0) * args.ldp;
+        const bf16_t* Q = args.Q + mat * args.q_mat + static_cast<int64_t>(j0) * args.ldq;
+        const int lr = lane / CPR, ls = lane % CPR;
 #pragma unroll
-        for (int c = 0; c < CH_P; ++c) {
-            const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-            regP[c] = *reinterpret_cast<const uint4*>(P + static_cast<int64_t>(row) * args.ldp + k0 + ch * 8);
+        for (int i = 0; i < IP; ++i) {
+            const int row = (wave * IP + i) * RPI + lr;
+            gp[i] = P + static_cast<int64_t>(row) * args.ldp + ((ls ^ swz<CPR>(row)) << 3);
         }
 #pragma unroll
-        for (int c = 0; c < CH_Q; ++c) {
-            const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-            regQ[c] = *reinterpret_cast<const uint4*>(Q + static_cast<int64_t>(row) * args.ldq + k0 + ch * 8);
+        for (int i = 0; i < IQ; ++i) {
+            const int row = (wave * IQ + i) * RPI + lr;
+            gq[i] = Q + static_cast<int64_t>(row) * args.ldq + ((ls ^ swz<CPR>(row)) << 3);
         }
+    }
+    // load L (< IP: P rows, else Q rows) of K step kt into LDS stage `stage`
+    auto issue_one = [&](int L, int kt, int stage) {
+        bf16_t* sP = lds + stage * STAGE;
+        const int k0 = kt * BK;
+        if (L < IP)
+            __builtin_amdgcn_global_load_lds((global_cptr)(gp[L] + k0),
+                                             (lds_ptr)(sP + (wave * IP + L) * RPI * BK), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((global_cptr)(gq[L - IP] + k0),
+                                             (lds_ptr)(sP + BM * BK + (wave * IQ + L - IP) * RPI * BK), 16, 0,
+                                             0);
     };
-    auto lstore = [&](int b) {
-        bf16_t* sP = lds[b];
-        bf16_t* sQ = lds[b] + BM * BK;
+
+    // ---- fragment reads: lane l reads row (l % 32) of a 32-row fragment,
+    // logical chunk 2 kk + l / 32, i.e. slot (2 kk + l / 32) ^ f(l % 32)
+    // (f depends on the row modulo 16 only, and fragments start at multiples
+    // of 32).
+    int soff[BK / 16];
+    {
+        const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
-        for (int c = 0; c < CH_P; ++c) {
-            const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4*>(sP + row * BK + ((ch ^ (row & 7)) << 3)) = regP[c];
-        }
-#pragma unroll
-        for (int c = 0; c < CH_Q; ++c) {
-            const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4*>(sQ + row * BK + ((ch ^ (row & 7)) << 3)) = regQ[c];
-        }
-    };
+        for (int kk = 0; kk < BK / 16; ++kk) soff[kk] = r * BK + (((2 * kk + hi) ^ swz<CPR>(r)) << 3);
+    }
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -102,37 +180,76 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
     const int nk = args.kpad / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const bf16_t* sP = lds[cur];
-        const bf16_t* sQ = lds[cur] + BM * BK;
+    // Every iteration issues the NLOAD loads of one K step (STAGES-1 steps
+    // ahead), so the number of loads outstanding behind step kt is always
+    // (STAGES-2)*NLOAD.  Steps past the end are clamped to the last one: they
+    // refill a stage that no later iteration reads.
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = kk * 2 + (lane >> 5);
-            bf16x8 a[FM], b[FN];
+    for (int s = 0; s < STAGES - 1; ++s) {
+        const int ks = s < nk ? s : nk - 1;
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int row = wm * WTM + fm * 32 + (lane & 31);
-                a[fm] = as_bf16x8(*reinterpret_cast<const uint4*>(sP + row * BK + ((ch ^ (row & 7)) << 3)));
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int row = wn * WTN + fn * 32 + (lane & 31);
-                b[fn] = as_bf16x8(*reinterpret_cast<const uint4*>(sQ + row * BK + ((ch ^ (row & 7)) << 3)));
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
-        }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
+        for (int L = 0; L < NLOAD; ++L) issue_one(L, ks, s);
     }
+
+    // Per K step: the MFMAs of slice kk (NMF of them) are interleaved with
+    // the LDS reads of slice kk+1's fragments and with this step's global->LDS
+    // loads, one instruction after another (full scheduling barriers keep the
+    // order), so the wave never stops issuing MFMAs for a burst of memory
+    // instructions.
+    constexpr int NKK = BK / 16;
+    constexpr int NMF = FM * FN;
+    constexpr int NR = FM + FN;                                  // fragment reads per slice
+    constexpr int RWIN = NMF * 3 / 4 > 0 ? NMF * 3 / 4 : 1;      // reads follow MFMAs 0 .. RWIN-1
+    constexpr int TOT = NKK * NMF;
+    constexpr int LWIN = STAGES == 2 ? (TOT / 2 > 0 ? TOT / 2 : 1) : (TOT * 3 / 4 > 0 ? TOT * 3 / 4 : 1);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm_barrier<(STAGES - 2) * NLOAD>();
+        // every wave is past step kt-1, so its stage can be refilled
+        const int kl = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
+        const int sl = (kt + STAGES - 1) % STAGES;
+
+        const bf16_t* sP = lds + (kt % STAGES) * STAGE + wm * WTM * BK;
+        const bf16_t* sQ = lds + (kt % STAGES) * STAGE + BM * BK + wn * WTN * BK;
+        bf16x8 a[2][FM], b[2][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            a[0][fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(sP + fm * 32 * BK + soff[0]));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            b[0][fn] = as_bf16x8(*reinterpret_cast<const u32x4*>(sQ + fn * 32 * BK + soff[0]));
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int c = kk & 1, n = c ^ 1;
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_barrier(0);
+                acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][q / FN], b[c][q % FN],
+                                                                              acc[q / FN][q % FN], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 < NKK) {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        if ((r * RWIN) / NR == q) {
+                            if (r < FM)
+                                a[n][r] = as_bf16x8(
+                                    *reinterpret_cast<const u32x4*>(sP + r * 32 * BK + soff[kk + 1]));
+                            else
+                                b[n][r - FM] = as_bf16x8(
+                                    *reinterpret_cast<const u32x4*>(sQ + (r - FM) * 32 * BK + soff[kk + 1]));
+                        }
+                    }
+                }
+                const int g = kk * NMF + q;
+#pragma unroll
+                for (int L = 0; L < NLOAD; ++L)
+                    if ((L * LWIN) / NLOAD == g) issue_one(L, kl, sl);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // drain the loads of the clamped tail steps before the epilogue
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue.  Accumulator register r of a 32x32 fragment holds, in
     // lane l, row 8*(r/4) + 4*(l/32) + r%4 and column l%32: each lane owns
@@ -147,69 +264,76 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int ib = i0 + wm * WTM + fm * 32 + 8 * g4 + 4 * (lane >> 5);
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = acc[fm][fn][4 * g4 + q];
-                if constexpr (KIND == GEMM_AAB) {
-                    // A is symmetric: A[i][j] = A[j][i], read along the contiguous run
-                    const bf16_t* e = args.E + cm * args.e_mat + static_cast<int64_t>(j) * args.lde + ib;
-                    const uint2 ev = *reinterpret_cast<const uint2*>(e);
-                    const bf16_t eh[4] = {static_cast<bf16_t>(ev.x & 0xffff), static_cast<bf16_t>(ev.x >> 16),
-                                          static_cast<bf16_t>(ev.y & 0xffff), static_cast<bf16_t>(ev.y >> 16)};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = fmaf(args.beta, v[q], args.alpha * bf16_to_f32(eh[q]));
-                } else if constexpr (KIND == GEMM_BX || KIND == GEMM_BX_FINAL) {
-                    // old X[i][j] read from X^T[j][i], which is the Q operand
-                    const bf16_t* e = args.E + cm * args.e_mat + static_cast<int64_t>(j) * args.lde + ib;
-                    const uint2 ev = *reinterpret_cast<const uint2*>(e);
-                    const bf16_t eh[4] = {static_cast<bf16_t>(ev.x & 0xffff), static_cast<bf16_t>(ev.x >> 16),
-                                          static_cast<bf16_t>(ev.y & 0xffff), static_cast<bf16_t>(ev.y >> 16)};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = fmaf(args.alpha, bf16_to_f32(eh[q]), v[q]);
+                float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
+                float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
+                if constexpr (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) {
+                    // AAB: A[i][j] = A[j][i] (symmetric); BX: old X[i][j] =
+                    // X^T[j][i].  Either way a contiguous run of 4 along i.
+                    const u32x2 ev = *reinterpret_cast<const u32x2*>(
+                        args.E + cm * args.e_mat + static_cast<int64_t>(j) * args.lde + ib);
+                    const float e0 = bf16_to_f32(static_cast<bf16_t>(ev.x & 0xffffu));
+                    const float e1 = bf16_to_f32(static_cast<bf16_t>(ev.x >> 16));
+                    const float e2 = bf16_to_f32(static_cast<bf16_t>(ev.y & 0xffffu));
+                    const float e3 = bf16_to_f32(static_cast<bf16_t>(ev.y >> 16));
+                    if constexpr (KIND == GEMM_AAB) {  // b A + c (A A)
+                        v0 = fmaf(args.beta, v0, args.alpha * e0);
+                        v1 = fmaf(args.beta, v1, args.alpha * e1);
+                        v2 = fmaf(args.beta, v2, args.alpha * e2);
+                        v3 = fmaf(args.beta, v3, args.alpha * e3);
+                    } else {  // a X + (B X)
+                        v0 = fmaf(args.alpha, e0, v0);
+                        v1 = fmaf(args.alpha, e1, v1);
+                        v2 = fmaf(args.alpha, e2, v2);
+                        v3 = fmaf(args.alpha, e3, v3);
+                    }
                 }
-                bf16_t h[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16(v[q]);
+                const bf16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+                const bf16_t h2 = f32_to_bf16(v2), h3 = f32_to_bf16(v3);
 
                 if constexpr (SYM) {
                     bf16_t* C = args.C + cm * args.c_mat;
                     if (!diag || ib + 3 <= j) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) C[static_cast<int64_t>(ib + q) * args.ldc + j] = h[q];
-                        uint2 pk;
-                        pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
-                        pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
-                        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(j) * args.ldc + ib) = pk;
+                        C[static_cast<int64_t>(ib + 0) * args.ldc + j] = h0;
+                        C[static_cast<int64_t>(ib + 1) * args.ldc + j] = h1;
+                        C[static_cast<int64_t>(ib + 2) * args.ldc + j] = h2;
+                        C[static_cast<int64_t>(ib + 3) * args.ldc + j] = h3;
+                        u32x2 pk;
+                        pk.x = pack2(h0, h1);
+                        pk.y = pack2(h2, h3);
+                        *reinterpret_cast<u32x2*>(C + static_cast<int64_t>(j) * args.ldc + ib) = pk;
                     } else {
+                        const bf16_t hv[4] = {h0, h1, h2, h3};
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             if (ib + q <= j) {
-                                C[static_cast<int64_t>(ib + q) * args.ldc + j] = h[q];
-                                C[static_cast<int64_t>(j) * args.ldc + ib + q] = h[q];
+                                C[static_cast<int64_t>(ib + q) * args.ldc + j] = hv[q];
+                                C[static_cast<int64_t>(j) * args.ldc + ib + q] = hv[q];
                             }
                         }
                     }
                 } else if constexpr (KIND == GEMM_BX) {
                     bf16_t* C = args.C + cm * args.c_mat;
                     bf16_t* CT = args.CT + cm * args.ct_mat;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) C[static_cast<int64_t>(ib + q) * args.ldc + j] = h[q];
-                    uint2 pk;
-                    pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
-                    pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
-                    *reinterpret_cast<uint2*>(CT + static_cast<int64_t>(j) * args.ldct + ib) = pk;
+                    C[static_cast<int64_t>(ib + 0) * args.ldc + j] = h0;
+                    C[static_cast<int64_t>(ib + 1) * args.ldc + j] = h1;
+                    C[static_cast<int64_t>(ib + 2) * args.ldc + j] = h2;
+                    C[static_cast<int64_t>(ib + 3) * args.ldc + j] = h3;
+                    u32x2 pk;
+                    pk.x = pack2(h0, h1);
+                    pk.y = pack2(h2, h3);
+                    *reinterpret_cast<u32x2*>(CT + static_cast<int64_t>(j) * args.ldct + ib) = pk;
                 } else {  // GEMM_BX_FINAL: float32 output in G's orientation
                     float* o = out.p[mat];
                     if (j < args.n) {
+                        const float f[4] = {bf16_to_f32(h0), bf16_to_f32(h1), bf16_to_f32(h2), bf16_to_f32(h3)};
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int i = ib + q;
                             if (i < args.m) {
-                                const float f = bf16_to_f32(h[q]);
                                 if (args.tall)
-                                    o[static_cast<int64_t>(j) * args.m + i] = f;
+                                    o[static_cast<int64_t>(j) * args.m + i] = f[q];
                                 else
-                                    o[static_cast<int64_t>(i) * args.n + j] = f;
+                                    o[static_cast<int64_t>(i) * args.n + j] = f[q];
                             }
                         }
                     }
@@ -219,16 +343,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
     }
 }
 
-template <int T>
+template <int BM, int BN, int BK, int STAGES>
 hipError_t launch_t(GemmKind kind, const GemmArgs& args, int cnt, const PtrTable* out, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(args.tiles_per_mat) * cnt);
     PtrTable o{};
     if (out) o = *out;
     switch (kind) {
-        case GEMM_SYRK: k_gemm_nt<T, GEMM_SYRK><<<grid, kThreads, 0, stream>>>(args, o); break;
-        case GEMM_AAB: k_gemm_nt<T, GEMM_AAB><<<grid, kThreads, 0, stream>>>(args, o); break;
-        case GEMM_BX: k_gemm_nt<T, GEMM_BX><<<grid, kThreads, 0, stream>>>(args, o); break;
-        case GEMM_BX_FINAL: k_gemm_nt<T, GEMM_BX_FINAL><<<grid, kThreads, 0, stream>>>(args, o); break;
+        case GEMM_SYRK: k_gemm_nt<BM, BM, BK, STAGES, GEMM_SYRK><<<grid, kThreads, 0, stream>>>(args, o); break;
+        case GEMM_AAB: k_gemm_nt<BM, BM, BK, STAGES, GEMM_AAB><<<grid, kThreads, 0, stream>>>(args, o); break;
+        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX><<<grid, kThreads, 0, stream>>>(args, o); break;
+        case GEMM_BX_FINAL:
+            k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX_FINAL><<<grid, kThreads, 0, stream>>>(args, o);
+            break;
     }
     return hipGetLastError();
 }
@@ -237,10 +363,23 @@ hipError_t launch_t(GemmKind kind, const GemmArgs& args, int cnt, const PtrTable
 
 hipError_t launch_gemm(GemmKind kind, int tile, const GemmArgs& args, int cnt, const PtrTable* out,
                        hipStream_t stream) {
-    switch (tile) {
-        case 64: return launch_t<64>(kind, args, cnt, out, stream);
-        case 128: return launch_t<128>(kind, args, cnt, out, stream);
-        case 256: return launch_t<256>(kind, args, cnt, out, stream);
+    // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages,
+    // 2 = BK 32 with 3 stages (MUON_GEMM_PIPE in the environment, for tuning)
+    static const int pipe = [] {
+        const char* s = getenv("MUON_GEMM_PIPE");
+        const int v = s ? atoi(s) : 0;
+        return (v >= 0 && v <= 2) ? v : 0;
+    }();
+    switch (tile * 4 + pipe) {
+        case 64 * 4 + 0: return launch_t<64, 64, 64, 2>(kind, args, cnt, out, stream);
+        case 64 * 4 + 1: return launch_t<64, 64, 32, 4>(kind, args, cnt, out, stream);
+        case 64 * 4 + 2: return launch_t<64, 64, 32, 3>(kind, args, cnt, out, stream);
+        case 128 * 4 + 0: return launch_t<128, 128, 64, 2>(kind, args, cnt, out, stream);
+        case 128 * 4 + 1: return launch_t<128, 128, 32, 4>(kind, args, cnt, out, stream);
+        case 128 * 4 + 2: return launch_t<128, 128, 32, 3>(kind, args, cnt, out, stream);
+        case 256 * 4 + 0: return launch_t<256, 256, 64, 2>(kind, args, cnt, out, stream);
+        case 256 * 4 + 1: return launch_t<256, 256, 32, 4>(kind, args, cnt, out, stream);
+        case 256 * 4 + 2: return launch_t<256, 256, 32, 3>(kind, args, cnt, out, stream);
         default: return hipErrorInvalidValue;
     }
 }

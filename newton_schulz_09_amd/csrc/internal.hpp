@@ -33,7 +33,11 @@ struct Ns5Plan {
     int mp, np;
     int nb;    // norm partials per matrix
     int cnt;   // matrices per pass
-    size_t x_elems, a_elems;           // per-matrix element counts
+    // row strides (elements) of X (mp rows), X^T (np rows) and A, B (mp rows):
+    // the padded widths plus a skew that keeps rows of power-of-two widths
+    // from all starting on the same memory channel
+    int ldx, ldxt, lda;
+    size_t x_elems, xt_elems, a_elems;  // per-matrix element counts
     size_t off_x[2], off_xt[2], off_a, off_b, off_part;  // byte offsets
     size_t bytes;
 };

@@ -59,10 +59,10 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(ConstPtrTable G, int64_t num
 
 constexpr int kCastTile = 64;
 
-__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int rows, int cols, int rows_pad,
-                                                         int cols_pad, int tiles_c, const double* partials,
-                                                         int nb, float eps, bf16_t* nat, int64_t nat_mat,
-                                                         bf16_t* tr, int64_t tr_mat) {
+__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int rows, int cols, int tiles_c,
+                                                         const double* partials, int nb, float eps, bf16_t* nat,
+                                                         int ld_nat, int64_t nat_mat, bf16_t* tr, int ld_tr,
+                                                         int64_t tr_mat) {
     const int mat = blockIdx.y;
     const int tr_i = blockIdx.x / tiles_c, tc_i = blockIdx.x % tiles_c;
     const int r0 = tr_i * kCastTile, c0 = tc_i * kCastTile;
@@ -93,18 +93,18 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int ro
         if (gr < rows && gc < cols) v = g[static_cast<int64_t>(gr) * cols + gc];
         const double q = static_cast<double>(bf16_to_f32(f32_to_bf16(v))) / d;
         const bf16_t h = (gr < rows && gc < cols) ? f64_to_bf16(q) : static_cast<bf16_t>(0);
-        natm[static_cast<int64_t>(gr) * cols_pad + gc] = h;
+        natm[static_cast<int64_t>(gr) * ld_nat + gc] = h;
         tile[r][c] = h;
     }
     __syncthreads();
     // transposed: lanes run along G's rows, which are the columns of tr
     const int r = lane;
     for (int cc = wave; cc < kCastTile; cc += kThreads / 64) {
-        trm[static_cast<int64_t>(c0 + cc) * rows_pad + r0 + r] = tile[r][cc];
+        trm[static_cast<int64_t>(c0 + cc) * ld_tr + r0 + r] = tile[r][cc];
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int cols_pad,
+__global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int ld_nat,
                                                        const bf16_t* nat, int64_t nat_mat) {
     const int mat = blockIdx.y;
     const int64_t total = static_cast<int64_t>(rows) * cols;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, i
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
         const int64_t r = i / cols, c = i - r * cols;
-        dst[i] = bf16_to_f32(src[r * cols_pad + c]);
+        dst[i] = bf16_to_f32(src[r * ld_nat + c]);
     }
 }
 
@@ -128,26 +128,30 @@ hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, 
 
 hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& plan, const double* partials,
                              float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream) {
-    // G's orientation: rows x cols padded; X is that orientation unless G is tall
+    // G's orientation is X's unless G is tall (then it is X^T's); both are
+    // written over their padded extent (padding as zeros)
     const int rows_pad = plan.tall ? plan.np : plan.mp;
     const int cols_pad = plan.tall ? plan.mp : plan.np;
+    const int ld_nat = plan.tall ? plan.ldxt : plan.ldx;
+    const int ld_tr = plan.tall ? plan.ldx : plan.ldxt;
+    const int64_t nat_mat = static_cast<int64_t>(plan.tall ? plan.xt_elems : plan.x_elems);
+    const int64_t tr_mat = static_cast<int64_t>(plan.tall ? plan.x_elems : plan.xt_elems);
     const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
-    const int64_t mat_elems = static_cast<int64_t>(plan.x_elems);
     k_scale_cast<<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
-        G, static_cast<int>(plan.rows), static_cast<int>(plan.cols), rows_pad, cols_pad, tiles_c, partials,
-        plan.nb, eps, nat, mat_elems, tr, mat_elems);
+        G, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb, eps, nat, ld_nat,
+        nat_mat, tr, ld_tr, tr_mat);
     return hipGetLastError();
 }
 
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
                            hipStream_t stream) {
-    const int cols_pad = plan.tall ? plan.mp : plan.np;
+    const int ld_nat = plan.tall ? plan.ldxt : plan.ldx;
+    const int64_t nat_mat = static_cast<int64_t>(plan.tall ? plan.xt_elems : plan.x_elems);
     const int64_t total = plan.rows * plan.cols;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 2048) blocks = 2048;
     k_copy_out<<<dim3(static_cast<unsigned>(blocks), cnt), kThreads, 0, stream>>>(
-        out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), cols_pad, nat,
-        static_cast<int64_t>(plan.x_elems));
+        out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), ld_nat, nat, nat_mat);
     return hipGetLastError();
 }
 
