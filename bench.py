@@ -47,7 +47,29 @@ def parse():
     p.add_argument("--skip-cpu-baseline", action="store_true")
     p.add_argument("--skip-square", action="store_true", help="skip the 4096x4096 NS5 line")
     p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device-to-device copy of COPY_BYTES bytes (10 times), the reference "
+                        "kernel whose FETCH_SIZE / WRITE_SIZE readings scale the traffic counters")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """A plain copy of a known size: 1 GiB read + 1 GiB written per launch."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(10):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / 10
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "ms": round(ms, 4),
+                      "GB/s (read+write)": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def time_step(st, steps, torch):
@@ -61,44 +83,37 @@ def time_step(st, steps, torch):
     return start.elapsed_time(stop) / steps
 
 
-def time_dominant_kernel(st, steps, torch, muon):
+def time_dominant_kernel(st, steps, torch):
     """Second timed pass: the same steps, with HIP events recorded by the
-    library around every a X + B X launch of NS5 steps 1-4."""
-    groups = list(st.groups.items())
-    pairs_per_call = st.steps - 1
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 * pairs_per_call)] for _ in groups]
-              for _ in range(steps)]
-    for per_step in events:                     # create the underlying HIP events
-        for evs in per_step:
-            for e in evs:
-                e.record()
+    library around every a X + B X launch of NS5 steps 1-4 (each launch covers
+    all 48 matrices)."""
+    max_pairs = 4 * (st.steps - 1)      # room for several launch groups
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * max_pairs)] for _ in range(steps)]
+    for evs in events:                  # create the underlying HIP events
+        for e in evs:
+            e.record()
     torch.cuda.synchronize()
-    flops_per_call, recorded = [], []
+    recorded = []
     for s in range(steps):
         st.momentum()
-        for gi, ((r, c), ix) in enumerate(groups):
-            muon.ns5_grouped([st.us[i] for i in ix], [st.outs[i] for i in ix], steps=st.steps, eps=st.eps,
-                             workspace=st.workspace, events=events[s][gi])
-            recorded.append(muon.ns5_grouped.last_recorded)
-            if s == 0:
-                m, n = min(r, c), max(r, c)
-                flops_per_call.append(len(ix) * 2.0 * m * m * n)
+        st.orthogonalise(events=events[s])
+        recorded.append(st.last_recorded())
     torch.cuda.synchronize()
-    total_ms, total_flops, launches = 0.0, 0.0, 0
-    k = 0
+    total_ms, launches = 0.0, 0
     for s in range(steps):
-        for gi in range(len(groups)):
-            evs = events[s][gi]
-            for p in range(recorded[k]):
-                total_ms += evs[2 * p].elapsed_time(evs[2 * p + 1])
-                total_flops += flops_per_call[gi]
-                launches += 1
-            k += 1
+        for p in range(recorded[s]):
+            total_ms += events[s][2 * p].elapsed_time(events[s][2 * p + 1])
+            launches += 1
+    groups_per_call = recorded[0] // (st.steps - 1)
+    if groups_per_call != 1:
+        raise RuntimeError(f"expected one launch group for the step, got {groups_per_call}")
+    flops_per_launch = sum(2.0 * min(r, c) ** 2 * max(r, c) for r, c in st.shapes)
     avg_ms = total_ms / launches
-    achieved = total_flops / (total_ms * 1e-3) / 1e12
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     return {
         "bound": "mfma",
-        "kernel": "k_gemm_nt<256, GEMM_BX>: X' = a X + B X (NS5 steps 1-4)",
+        "kernel": "k_gemm_nt<128, 128, 64, 2, GEMM_BX>: X' = a X + B X of NS5 steps 1-4, one launch over all "
+                  "48 matrices",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -106,7 +121,7 @@ def time_dominant_kernel(st, steps, torch, muon):
         "traffic": None,
         "launches": launches,
         "avg_launch_us": round(avg_ms * 1e3, 2),
-        "flops_per_launch": total_flops / launches,
+        "flops_per_launch": flops_per_launch,
     }
 
 
@@ -144,25 +159,22 @@ def time_square(torch, muon, workloads, reps=10):
 
 
 def cpu_baseline(items):
-    """The oracle, as it stands, on layer 0's four matrices (one of each
-    shape): momentum then NS5, timed on this host's cores."""
-    import numpy as np
+    """The oracle, as it stands, on the whole step (all 48 matrices: momentum
+    then NS5), timed on this host's cores."""
     import threadpoolctl
 
     import oracle
-    sample = [it for it in items if it[0] == 0]
-    flops = sum(oracle.ns5_nominal_flops(*it[2].shape) for it in sample)
+    flops = sum(oracle.ns5_nominal_flops(*it[2].shape) for it in items)
     t0 = time.perf_counter()
-    for _, _, G, buf in sample:
+    for _, _, G, buf in items:
         _, u = oracle.momentum_nesterov(G, buf, 0.95)
         oracle.ns5(u)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    del np
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "layer 0 of the GPT-2 124M set (768x2304, 768x768, 768x3072, 3072x768): momentum + NS5, "
-                      f"{flops:.3g} nominal NS5 flops in {dt:.1f} s (float64 BLAS matmuls, single-threaded "
-                      "bf16 rounding)"}
+            "sample": f"the whole GPT-2 124M step (48 matrices, momentum + NS5) once: {flops:.4g} nominal NS5 "
+                      f"flops in {dt:.1f} s, {dt * 1e3:.0f} ms per step (float64 BLAS matmuls on {threads} "
+                      "threads, bf16 rounding in numpy)"}
 
 
 def main():
@@ -174,9 +186,13 @@ def main():
         sys.exit(2)
     import torch
 
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
     from newton_schulz_09_amd import muon, step, workloads
 
-    torch.cuda.set_device(0)
     t0 = time.time()
     items = workloads.gpt2_124m()
     st = step.MuonStep([it[2].shape for it in items], device="cuda:0")
@@ -220,7 +236,7 @@ def main():
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
     }
     if not args.skip_extras:
-        res["roofline"] = time_dominant_kernel(st, args.steps, torch, muon)
+        res["roofline"] = time_dominant_kernel(st, args.steps, torch)
         log(f"dominant kernel: {res['roofline']}")
         res["momentum"] = time_momentum(st, args.steps, torch)
         log(f"momentum: {res['momentum']}")

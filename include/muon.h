@@ -51,9 +51,8 @@ typedef enum muon_status {
 #define MUON_NS5_DEFAULT_STEPS 5
 #define MUON_NS5_DEFAULT_EPS 1e-7f
 
-/* Largest number of matrices one grouped call processes in a single pass;
- * larger groups are processed in passes of this many, reusing the
- * workspace. */
+/* Largest number of matrices one launch covers; larger groups and batches
+ * are processed in passes of at most this many, reusing the workspace. */
 #define MUON_NS5_MAX_GROUP 128
 /* Largest supported min(rows, cols) and max(rows, cols). */
 #define MUON_NS5_MAX_SHORT 16384
@@ -79,8 +78,8 @@ int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, 
 
 /*
  * Bytes of workspace muon_ns5 / muon_ns5_grouped need for `count` matrices of
- * rows x cols (count is capped at MUON_NS5_MAX_GROUP, since larger groups
- * reuse one pass's workspace).  Returns 0 for invalid sizes.  The workspace
+ * rows x cols (larger groups than MUON_NS5_MAX_GROUP reuse one pass's
+ * workspace, so the size stops growing there).  Returns 0 for invalid sizes.  The workspace
  * must be device memory aligned to 256 bytes; its contents on entry do not
  * matter.
  */
@@ -126,19 +125,48 @@ int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, in
                      void* stream);
 
 /*
- * Measurement support: exactly muon_ns5_grouped, and in addition records
- * caller-created hipEvent_t pairs on `stream` around launches of the
+ * Bytes of workspace muon_ns5_batched needs for `count` matrices of shapes
+ * rows[i] x cols[i].  Returns 0 for invalid sizes (a null array, count < 1,
+ * a dimension < 1 or beyond the limits).  Same alignment rule as above.
+ */
+size_t muon_ns5_batched_workspace_size(const int64_t* rows, const int64_t* cols, int64_t count);
+
+/*
+ * NS5 of `count` independent matrices of arbitrary shapes, each exactly as
+ * muon_ns5 computes it.  Matrices of equal shape are batched together, and
+ * every product of every NS5 step is one launch over all matrices whose
+ * short side takes the same tile size (up to MUON_NS5_MAX_GROUP matrices and
+ * 8 distinct shapes per launch; beyond that the batch runs in passes that
+ * reuse the workspace).  Use this for a whole optimizer step: the launches
+ * are few and large instead of many and small.
+ *  G, out     : host arrays of `count` device pointers (float32, row-major
+ *               rows[i] x cols[i]); out[i] may alias G[i]; distinct i must not
+ *               overlap.
+ *  rows, cols : host arrays of `count` sizes, each >= 1 and within the
+ *               limits of muon_ns5.
+ *  count      : >= 1.
+ *  steps, eps, stream : as in muon_ns5.
+ *  workspace, workspace_bytes: >= muon_ns5_batched_workspace_size(rows, cols,
+ *               count).
+ * Errors: as muon_ns5_grouped, per matrix.
+ */
+int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                     int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Measurement support: exactly muon_ns5_batched, and in addition records
+ * caller-created hipEvent_t pairs on `stream` around the launches of the
  * a X + B X product of the non-final steps (the dominant kernel of the
  * iteration): events[2*i] just before and events[2*i+1] just after the i-th
  * such launch, for i < n_event_pairs.  *recorded (if non-null) receives the
- * number of pairs recorded.  With events == NULL it is muon_ns5_grouped.
- * Errors: as muon_ns5_grouped, plus MUON_ERR_INVALID_ARG for
+ * number of pairs recorded.  With events == NULL it is muon_ns5_batched.
+ * Errors: as muon_ns5_batched, plus MUON_ERR_INVALID_ARG for
  * n_event_pairs < 0 or events == NULL with n_event_pairs > 0.
  */
-int muon_ns5_grouped_timed(const float* const* G, float* const* out, int64_t count, int64_t rows,
-                           int64_t cols, int steps, float eps, void* workspace,
-                           size_t workspace_bytes, void* stream, void* const* events,
-                           int n_event_pairs, int* recorded);
+int muon_ns5_batched_timed(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                           int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events, int n_event_pairs, int* recorded);
 
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* muon_status_string(int status);

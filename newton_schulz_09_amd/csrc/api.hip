@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/muon.h"
 #include "internal.hpp"
@@ -123,94 +124,206 @@ struct EventSink {
     int recorded = 0;
 };
 
-int run_ns5(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols, int steps,
-            float eps, void* ws, size_t ws_bytes, hipStream_t stream, EventSink* sink) {
-    if (rows < 1 || cols < 1) return fail(MUON_ERR_INVALID_ARG, "rows and cols must be >= 1 (got %lld x %lld)",
-                                          (long long)rows, (long long)cols);
+// A set of same-shaped matrices of one call.
+struct Segment {
+    int64_t rows, cols, count;
+    const float* const* G;
+    float* const* out;
+};
+
+// Up to kMaxGroup matrices of one segment, with its workspace layout at byte
+// offset `base` of its launch group's workspace.
+struct Chunk {
+    const float* const* G;
+    float* const* out;
+    Ns5Plan plan;
+    size_t base;
+};
+
+// Chunks that share the tile size: each GEMM of each NS5 step is a single
+// launch over all of them.  Groups run one after another, each reusing the
+// workspace from its start.
+struct Group {
+    std::vector<Chunk> chunks;
+    int tile = 0;
+    int mats = 0;
+    int64_t bx_blocks = 0;  // workgroups of the largest launch (a X + B X)
+    size_t bytes = 0;
+};
+
+int64_t bx_blocks(const Ns5Plan& p) {
+    return static_cast<int64_t>(p.mp / p.tile) * (p.np / p.tile) * p.cnt;
+}
+
+// Splits validated segments into launch groups (deterministic in the shapes,
+// so the workspace query and the call agree).
+int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups) {
+    groups->clear();
+    for (int si = 0; si < nseg; ++si) {
+        const Segment& sg = segs[si];
+        for (int64_t start = 0; start < sg.count;) {
+            Ns5Plan pl;
+            if (!make_plan(sg.rows, sg.cols, sg.count - start, &pl))
+                return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits",
+                            (long long)sg.rows, (long long)sg.cols);
+            Group* g = groups->empty() ? nullptr : &groups->back();
+            if (!g || g->tile != pl.tile || g->mats + pl.cnt > kMaxGroup ||
+                static_cast<int>(g->chunks.size()) == kMaxSeg || g->bx_blocks + bx_blocks(pl) > kMaxWorkgroups) {
+                groups->emplace_back();
+                g = &groups->back();
+                g->tile = pl.tile;
+            }
+            Chunk c;
+            c.G = sg.G ? sg.G + start : nullptr;
+            c.out = sg.out ? sg.out + start : nullptr;
+            c.plan = pl;
+            c.base = g->bytes;
+            g->chunks.push_back(c);
+            g->mats += pl.cnt;
+            g->bx_blocks += bx_blocks(pl);
+            g->bytes += pl.bytes;
+            start += pl.cnt;
+        }
+    }
+    return MUON_OK;
+}
+
+size_t groups_bytes(const std::vector<Group>& groups) {
+    size_t b = 0;
+    for (const Group& g : groups) b = g.bytes > b ? g.bytes : b;
+    return b;
+}
+
+int check_common(int steps, float eps) {
     if (steps < 0) return fail(MUON_ERR_INVALID_ARG, "steps must be >= 0 (got %d)", steps);
     if (!isfinite(eps)) return fail(MUON_ERR_INVALID_ARG, "eps must be finite");
-    for (int64_t i = 0; i < count; ++i) {
-        if (!G[i] || !out[i]) return fail(MUON_ERR_INVALID_ARG, "null matrix pointer at index %lld", (long long)i);
-    }
-    Ns5Plan plan;
-    if (!make_plan(rows, cols, count, &plan))
-        return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits", (long long)rows,
-                    (long long)cols);
+    return MUON_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, size_t need) {
     if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is null");
     if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-    if (ws_bytes < plan.bytes)
-        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, plan.bytes);
+    if (ws_bytes < need) return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return MUON_OK;
+}
 
+// Workspace pointers of one chunk.
+struct ChunkBufs {
+    bf16_t *X[2], *XT[2], *A, *B;
+    double* part;
+};
+
+ChunkBufs bufs_of(char* ws, const Chunk& c) {
+    char* b = ws + c.base;
+    const Ns5Plan& p = c.plan;
+    ChunkBufs r;
+    r.X[0] = reinterpret_cast<bf16_t*>(b + p.off_x[0]);
+    r.X[1] = reinterpret_cast<bf16_t*>(b + p.off_x[1]);
+    r.XT[0] = reinterpret_cast<bf16_t*>(b + p.off_xt[0]);
+    r.XT[1] = reinterpret_cast<bf16_t*>(b + p.off_xt[1]);
+    r.A = reinterpret_cast<bf16_t*>(b + p.off_a);
+    r.B = reinterpret_cast<bf16_t*>(b + p.off_b);
+    r.part = reinterpret_cast<double*>(b + p.off_part);
+    return r;
+}
+
+// The launch sequence: per chunk the norm and the bf16 cast, then per NS5
+// step one launch per product over every chunk of the group.
+int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws, hipStream_t stream,
+               EventSink* sink) {
     (void)hipGetLastError();  // start from a clean error state
-    char* base = static_cast<char*>(ws);
-    bf16_t* X[2] = {reinterpret_cast<bf16_t*>(base + plan.off_x[0]), reinterpret_cast<bf16_t*>(base + plan.off_x[1])};
-    bf16_t* XT[2] = {reinterpret_cast<bf16_t*>(base + plan.off_xt[0]),
-                     reinterpret_cast<bf16_t*>(base + plan.off_xt[1])};
-    bf16_t* A = reinterpret_cast<bf16_t*>(base + plan.off_a);
-    bf16_t* B = reinterpret_cast<bf16_t*>(base + plan.off_b);
-    double* part = reinterpret_cast<double*>(base + plan.off_part);
-    const int T = plan.tile;
-    const int tiles_m = plan.mp / T, tiles_n = plan.np / T;
-    const int64_t xe = static_cast<int64_t>(plan.x_elems), xte = static_cast<int64_t>(plan.xt_elems);
-    const int64_t ae = static_cast<int64_t>(plan.a_elems);
+    for (const Group& grp : groups) {
+        const int nseg = static_cast<int>(grp.chunks.size());
+        PtrTable out_all{};
+        int out_base[kMaxSeg];
+        {
+            int k = 0;
+            for (int ci = 0; ci < nseg; ++ci) {
+                out_base[ci] = k;
+                for (int i = 0; i < grp.chunks[ci].plan.cnt; ++i) out_all.p[k++] = grp.chunks[ci].out[i];
+            }
+        }
+        for (int ci = 0; ci < nseg; ++ci) {
+            const Chunk& c = grp.chunks[ci];
+            const Ns5Plan& pl = c.plan;
+            ChunkBufs b = bufs_of(ws, c);
+            ConstPtrTable gt{};
+            for (int i = 0; i < pl.cnt; ++i) gt.p[i] = c.G[i];
+            hipError_t e = launch_sumsq(gt, pl.cnt, pl.rows * pl.cols, pl.nb, b.part, stream);
+            if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
+            bf16_t* nat = pl.tall ? b.XT[0] : b.X[0];
+            bf16_t* tr = pl.tall ? b.X[0] : b.XT[0];
+            e = launch_scale_cast(gt, pl.cnt, pl, b.part, eps, nat, tr, stream);
+            if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
+            if (steps == 0) {
+                PtrTable ot{};
+                for (int i = 0; i < pl.cnt; ++i) ot.p[i] = c.out[i];
+                e = launch_copy_out(pl, pl.cnt, nat, ot, stream);
+                if (e != hipSuccess) return hip_fail(e, "copy-out launch");
+            }
+        }
+        if (steps == 0) continue;
 
-    for (int64_t start = 0; start < count; start += plan.cnt) {
-        const int cnt = static_cast<int>(count - start < plan.cnt ? count - start : plan.cnt);
-        ConstPtrTable gt{};
-        PtrTable ot{};
-        for (int i = 0; i < cnt; ++i) {
-            gt.p[i] = G[start + i];
-            ot.p[i] = out[start + i];
-        }
-        hipError_t e = launch_sumsq(gt, cnt, rows * cols, plan.nb, part, stream);
-        if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
-        bf16_t* nat = plan.tall ? XT[0] : X[0];
-        bf16_t* tr = plan.tall ? X[0] : XT[0];
-        e = launch_scale_cast(gt, cnt, plan, part, eps, nat, tr, stream);
-        if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
-        if (steps == 0) {
-            e = launch_copy_out(plan, cnt, nat, ot, stream);
-            if (e != hipSuccess) return hip_fail(e, "copy-out launch");
-            continue;
-        }
         int cur = 0;
         for (int s = 0; s < steps; ++s) {
             const int nxt = cur ^ 1;
             const bool last = (s == steps - 1);
-            GemmArgs g{};
-            // A = X X^T
-            g.P = X[cur]; g.p_mat = xe; g.ldp = plan.ldx;
-            g.Q = X[cur]; g.q_mat = xe; g.ldq = plan.ldx;
-            g.kpad = static_cast<int>(round_up(plan.n, 64));
-            g.tiles = tiles_m; g.tiles_n = tiles_m; g.tiles_per_mat = tiles_m * (tiles_m + 1) / 2;
-            g.C = A; g.c_mat = ae; g.ldc = plan.lda;
-            e = launch_gemm(GEMM_SYRK, T, g, cnt, nullptr, stream);
+            GemmLaunch syrk{}, aab{}, bx{};
+            syrk.nseg = aab.nseg = bx.nseg = nseg;
+            int nb_sym = 0, nb_bx = 0;
+            for (int ci = 0; ci < nseg; ++ci) {
+                const Chunk& c = grp.chunks[ci];
+                const Ns5Plan& pl = c.plan;
+                ChunkBufs b = bufs_of(ws, c);
+                const int T = pl.tile;
+                const int tiles_m = pl.mp / T, tiles_n = pl.np / T;
+                const int64_t xe = static_cast<int64_t>(pl.x_elems), xte = static_cast<int64_t>(pl.xt_elems);
+                const int64_t ae = static_cast<int64_t>(pl.a_elems);
+                // A = X X^T
+                GemmArgs& g1 = syrk.seg[ci];
+                g1.first_block = nb_sym;
+                g1.out_base = out_base[ci];
+                g1.P = b.X[cur]; g1.p_mat = xe; g1.ldp = pl.ldx;
+                g1.Q = b.X[cur]; g1.q_mat = xe; g1.ldq = pl.ldx;
+                g1.kpad = static_cast<int>(round_up(pl.n, 64));
+                g1.tiles = tiles_m; g1.tiles_n = tiles_m; g1.tiles_per_mat = tiles_m * (tiles_m + 1) / 2;
+                g1.C = b.A; g1.c_mat = ae; g1.ldc = pl.lda;
+                g1.m = pl.m; g1.n = pl.n; g1.tall = pl.tall ? 1 : 0;
+                // B = b A + c A A  (same triangle of tiles)
+                GemmArgs& g2 = aab.seg[ci];
+                g2 = g1;
+                g2.P = b.A; g2.p_mat = ae; g2.ldp = pl.lda;
+                g2.Q = b.A; g2.q_mat = ae; g2.ldq = pl.lda;
+                g2.kpad = static_cast<int>(round_up(pl.m, 64));
+                g2.C = b.B; g2.c_mat = ae; g2.ldc = pl.lda;
+                g2.E = b.A; g2.e_mat = ae; g2.lde = pl.lda;
+                g2.alpha = MUON_NS5_B; g2.beta = MUON_NS5_C;
+                nb_sym += g1.tiles_per_mat * pl.cnt;
+                // X' = a X + B X
+                GemmArgs& g3 = bx.seg[ci];
+                g3.first_block = nb_bx;
+                g3.out_base = out_base[ci];
+                g3.P = b.B; g3.p_mat = ae; g3.ldp = pl.lda;
+                g3.Q = b.XT[cur]; g3.q_mat = xte; g3.ldq = pl.ldxt;
+                g3.kpad = static_cast<int>(round_up(pl.m, 64));
+                g3.tiles = tiles_m; g3.tiles_n = tiles_n; g3.tiles_per_mat = tiles_m * tiles_n;
+                g3.E = b.XT[cur]; g3.e_mat = xte; g3.lde = pl.ldxt;
+                g3.alpha = MUON_NS5_A; g3.beta = 1.0f;
+                g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
+                g3.CT = b.XT[nxt]; g3.ct_mat = xte; g3.ldct = pl.ldxt;
+                g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
+                nb_bx += g3.tiles_per_mat * pl.cnt;
+            }
+            hipError_t e = launch_gemm(GEMM_SYRK, grp.tile, syrk, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
-            // B = b A + c A A
-            g.P = A; g.p_mat = ae; g.ldp = plan.lda;
-            g.Q = A; g.q_mat = ae; g.ldq = plan.lda;
-            g.kpad = static_cast<int>(round_up(plan.m, 64));
-            g.C = B; g.c_mat = ae; g.ldc = plan.lda;
-            g.E = A; g.e_mat = ae; g.lde = plan.lda;
-            g.alpha = MUON_NS5_B; g.beta = MUON_NS5_C;
-            e = launch_gemm(GEMM_AAB, T, g, cnt, nullptr, stream);
+            e = launch_gemm(GEMM_AAB, grp.tile, aab, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");
-            // X' = a X + B X
-            g.P = B; g.p_mat = ae; g.ldp = plan.lda;
-            g.Q = XT[cur]; g.q_mat = xte; g.ldq = plan.ldxt;
-            g.kpad = static_cast<int>(round_up(plan.m, 64));
-            g.tiles = tiles_m; g.tiles_n = tiles_n; g.tiles_per_mat = tiles_m * tiles_n;
-            g.E = XT[cur]; g.e_mat = xte; g.lde = plan.ldxt;
-            g.alpha = MUON_NS5_A; g.beta = 1.0f;
-            g.C = X[nxt]; g.c_mat = xe; g.ldc = plan.ldx;
-            g.CT = XT[nxt]; g.ct_mat = xte; g.ldct = plan.ldxt;
-            g.m = plan.m; g.n = plan.n; g.tall = plan.tall ? 1 : 0;
             const bool timed = sink && !last && sink->recorded < sink->pairs;
             if (timed) {
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded]), stream);
                 if (e != hipSuccess) return hip_fail(e, "event record");
             }
-            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, T, g, cnt, last ? &ot : nullptr, stream);
+            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, grp.tile, bx, nb_bx, last ? &out_all : nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "a X + B X launch");
             if (timed) {
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded + 1]), stream);
@@ -221,6 +334,91 @@ int run_ns5(const float* const* G, float* const* out, int64_t count, int64_t row
         }
     }
     return ok();
+}
+
+// Same-shape matrices of a grouped call, validated.
+int grouped_segment(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
+                    Segment* seg) {
+    if (!G || !out) return fail(MUON_ERR_INVALID_ARG, "null pointer array");
+    if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count must be >= 1 (got %lld)", (long long)count);
+    if (rows < 1 || cols < 1)
+        return fail(MUON_ERR_INVALID_ARG, "rows and cols must be >= 1 (got %lld x %lld)", (long long)rows,
+                    (long long)cols);
+    for (int64_t i = 0; i < count; ++i)
+        if (!G[i] || !out[i]) return fail(MUON_ERR_INVALID_ARG, "null matrix pointer at index %lld", (long long)i);
+    seg->rows = rows;
+    seg->cols = cols;
+    seg->count = count;
+    seg->G = G;
+    seg->out = out;
+    return MUON_OK;
+}
+
+// A mixed-shape batch bucketed into segments by shape (in order of first
+// appearance), with per-segment pointer arrays held in `gs` / `os`.
+int batched_segments(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                     int64_t count, bool need_ptrs, std::vector<Segment>* segs,
+                     std::vector<std::vector<const float*>>* gs, std::vector<std::vector<float*>>* os) {
+    if (!rows || !cols) return fail(MUON_ERR_INVALID_ARG, "null shape array");
+    if (need_ptrs && (!G || !out)) return fail(MUON_ERR_INVALID_ARG, "null pointer array");
+    if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count must be >= 1 (got %lld)", (long long)count);
+    std::vector<int64_t> key_r, key_c;
+    std::vector<int> which(static_cast<size_t>(count));
+    for (int64_t i = 0; i < count; ++i) {
+        if (rows[i] < 1 || cols[i] < 1)
+            return fail(MUON_ERR_INVALID_ARG, "matrix %lld: rows and cols must be >= 1 (got %lld x %lld)",
+                        (long long)i, (long long)rows[i], (long long)cols[i]);
+        if (need_ptrs && (!G[i] || !out[i]))
+            return fail(MUON_ERR_INVALID_ARG, "null matrix pointer at index %lld", (long long)i);
+        int k = 0;
+        while (k < static_cast<int>(key_r.size()) && !(key_r[k] == rows[i] && key_c[k] == cols[i])) ++k;
+        if (k == static_cast<int>(key_r.size())) {
+            key_r.push_back(rows[i]);
+            key_c.push_back(cols[i]);
+        }
+        which[static_cast<size_t>(i)] = k;
+    }
+    const size_t nk = key_r.size();
+    gs->assign(nk, {});
+    os->assign(nk, {});
+    std::vector<int64_t> cnt(nk, 0);
+    for (int64_t i = 0; i < count; ++i) {
+        const int k = which[static_cast<size_t>(i)];
+        ++cnt[k];
+        if (need_ptrs) {
+            (*gs)[k].push_back(G[i]);
+            (*os)[k].push_back(out[i]);
+        }
+    }
+    segs->clear();
+    for (size_t k = 0; k < nk; ++k) {
+        Segment sg;
+        sg.rows = key_r[k];
+        sg.cols = key_c[k];
+        sg.count = cnt[k];
+        sg.G = need_ptrs ? (*gs)[k].data() : nullptr;
+        sg.out = need_ptrs ? (*os)[k].data() : nullptr;
+        segs->push_back(sg);
+    }
+    return MUON_OK;
+}
+
+int run_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                int64_t count, int steps, float eps, void* ws, size_t ws_bytes, hipStream_t stream,
+                EventSink* sink) {
+    int st = check_common(steps, eps);
+    if (st) return st;
+    std::vector<Segment> segs;
+    std::vector<std::vector<const float*>> gs;
+    std::vector<std::vector<float*>> os;
+    st = batched_segments(G, out, rows, cols, count, true, &segs, &gs, &os);
+    if (st) return st;
+    std::vector<Group> groups;
+    st = plan_groups(segs.data(), static_cast<int>(segs.size()), &groups);
+    if (st) return st;
+    st = check_workspace(ws, ws_bytes, groups_bytes(groups));
+    if (st) return st;
+    return run_groups(groups, steps, eps, static_cast<char*>(ws), stream, sink);
 }
 
 }  // namespace
@@ -242,42 +440,71 @@ int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, 
 }
 
 size_t muon_ns5_workspace_size(int64_t rows, int64_t cols, int64_t count) {
-    muon::Ns5Plan plan;
-    if (!muon::make_plan(rows, cols, count, &plan)) return 0;
-    return plan.bytes;
+    using namespace muon;
+    if (rows < 1 || cols < 1 || count < 1) return 0;
+    Segment sg{rows, cols, count, nullptr, nullptr};
+    std::vector<Group> groups;
+    const std::string saved = g_last_error;
+    const int st = plan_groups(&sg, 1, &groups);
+    g_last_error = saved;
+    return st ? 0 : groups_bytes(groups);
+}
+
+size_t muon_ns5_batched_workspace_size(const int64_t* rows, const int64_t* cols, int64_t count) {
+    using namespace muon;
+    const std::string saved = g_last_error;
+    std::vector<Segment> segs;
+    std::vector<std::vector<const float*>> gs;
+    std::vector<std::vector<float*>> os;
+    std::vector<Group> groups;
+    int st = batched_segments(nullptr, nullptr, rows, cols, count, false, &segs, &gs, &os);
+    if (!st) st = plan_groups(segs.data(), static_cast<int>(segs.size()), &groups);
+    g_last_error = saved;
+    return st ? 0 : groups_bytes(groups);
 }
 
 int muon_ns5(const float* G, float* out, int64_t rows, int64_t cols, int steps, float eps, void* workspace,
              size_t workspace_bytes, void* stream) {
     using namespace muon;
     if (!G || !out) return fail(MUON_ERR_INVALID_ARG, "null G or out");
-    return run_ns5(&G, &out, 1, rows, cols, steps, eps, workspace, workspace_bytes,
-                   static_cast<hipStream_t>(stream), nullptr);
+    return muon_ns5_grouped(&G, &out, 1, rows, cols, steps, eps, workspace, workspace_bytes, stream);
 }
 
 int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
                      int steps, float eps, void* workspace, size_t workspace_bytes, void* stream) {
     using namespace muon;
-    if (!G || !out) return fail(MUON_ERR_INVALID_ARG, "null pointer array");
-    if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count must be >= 1 (got %lld)", (long long)count);
-    return run_ns5(G, out, count, rows, cols, steps, eps, workspace, workspace_bytes,
-                   static_cast<hipStream_t>(stream), nullptr);
+    Segment sg;
+    int st = grouped_segment(G, out, count, rows, cols, &sg);
+    if (st) return st;
+    st = check_common(steps, eps);
+    if (st) return st;
+    std::vector<Group> groups;
+    st = plan_groups(&sg, 1, &groups);
+    if (st) return st;
+    st = check_workspace(workspace, workspace_bytes, groups_bytes(groups));
+    if (st) return st;
+    return run_groups(groups, steps, eps, static_cast<char*>(workspace), static_cast<hipStream_t>(stream), nullptr);
 }
 
-int muon_ns5_grouped_timed(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
-                           int steps, float eps, void* workspace, size_t workspace_bytes, void* stream,
-                           void* const* events, int n_event_pairs, int* recorded) {
+int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                     int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    return run_batched(G, out, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), nullptr);
+}
+
+int muon_ns5_batched_timed(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                           int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events, int n_event_pairs, int* recorded) {
     using namespace muon;
     if (recorded) *recorded = 0;
-    if (!G || !out) return fail(MUON_ERR_INVALID_ARG, "null pointer array");
-    if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count must be >= 1 (got %lld)", (long long)count);
     if (n_event_pairs < 0 || (!events && n_event_pairs > 0))
         return fail(MUON_ERR_INVALID_ARG, "bad event array");
     EventSink sink;
     sink.events = events;
     sink.pairs = events ? n_event_pairs : 0;
-    const int st = run_ns5(G, out, count, rows, cols, steps, eps, workspace, workspace_bytes,
-                           static_cast<hipStream_t>(stream), &sink);
+    const int st = run_batched(G, out, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                               static_cast<hipStream_t>(stream), &sink);
     if (recorded) *recorded = sink.recorded;
     return st;
 }

@@ -30,8 +30,9 @@
 // consecutive rows, one chunk each, 16 bytes per lane) over all banks whether
 // the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
 //
-// Work distribution: one workgroup per output tile, every matrix of a group
-// in the same launch.  Consecutive workgroups are dispatched round-robin over
+// Work distribution: one workgroup per output tile, every matrix of every
+// segment (a set of same-shaped matrices; up to kMaxSeg shapes that share the
+// tile size) in the same launch.  Consecutive workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so the workgroup index is remapped to
 // give every XCD a contiguous range of tiles; within a matrix, tiles of the
 // full grid are ordered in bands of kBand tile rows (column by column inside
@@ -82,7 +83,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 template <int BM, int BN, int BK, int STAGES, int KIND>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable out) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
     static_assert(!SYM || BM == BN, "symmetric products use square tiles");
     static_assert(BK == 64 || BK == 32, "BK is 32 or 64");
@@ -96,13 +97,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
     constexpr int NLOAD = IP + IQ;
     constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
     static_assert(IP >= 1 && IQ >= 1, "tile too small for the loader");
+    static_assert(BM * BN <= STAGES * STAGE, "the epilogue reuses the stages as four wave sub-tiles");
 
     __shared__ __attribute__((aligned(1024))) bf16_t lds[STAGES * STAGE];
 
-    // ---- which matrix and which output tile
+    // ---- which segment, which matrix and which output tile
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
-    const int mat = lid / args.tiles_per_mat;
-    int t = lid - mat * args.tiles_per_mat;
+    int si = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxSeg; ++q)
+        if (q < launch.nseg && lid >= launch.seg[q].first_block) si = q;
+    const GemmArgs& args = launch.seg[si];
+    const int local = lid - args.first_block;
+    const int mat = local / args.tiles_per_mat;
+    int t = local - mat * args.tiles_per_mat;
     int ti, tj;
     if constexpr (SYM) {
         ti = 0;
@@ -253,17 +261,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
 
     // ---- epilogue.  Accumulator register r of a 32x32 fragment holds, in
     // lane l, row 8*(r/4) + 4*(l/32) + r%4 and column l%32: each lane owns
-    // runs of 4 consecutive rows in one column.
-    const bool diag = SYM && (ti == tj);
+    // runs of 4 consecutive rows in one column.  The fused update is applied
+    // in registers and rounded once to bf16; then every wave passes its
+    // (WTM x WTN) sub-tile through its own LDS region to store whole rows with
+    // 16-byte stores: once transposed (X^T for the a X + B X product, the
+    // mirror block for the symmetric ones) and once as is.
     const int64_t cm = static_cast<int64_t>(mat);
+    const int i0w = i0 + wm * WTM, j0w = j0 + wn * WTN;  // this wave's sub-tile origin
+    u32x2 hv[FM][FN][4];                                  // 4 bf16 (rows ib..ib+3, column j)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int j = j0 + wn * WTN + fn * 32 + (lane & 31);
+            const int j = j0w + fn * 32 + (lane & 31);
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int ib = i0 + wm * WTM + fm * 32 + 8 * g4 + 4 * (lane >> 5);
+                const int ib = i0w + fm * 32 + 8 * g4 + 4 * (lane >> 5);
                 float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
                 float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
                 if constexpr (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) {
@@ -287,73 +300,139 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmArgs args, PtrTable
                         v3 = fmaf(args.alpha, e3, v3);
                     }
                 }
-                const bf16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-                const bf16_t h2 = f32_to_bf16(v2), h3 = f32_to_bf16(v3);
+                hv[fm][fn][g4].x = pack2(f32_to_bf16(v0), f32_to_bf16(v1));
+                hv[fm][fn][g4].y = pack2(f32_to_bf16(v2), f32_to_bf16(v3));
+            }
+        }
+    }
 
-                if constexpr (SYM) {
-                    bf16_t* C = args.C + cm * args.c_mat;
-                    if (!diag || ib + 3 <= j) {
-                        C[static_cast<int64_t>(ib + 0) * args.ldc + j] = h0;
-                        C[static_cast<int64_t>(ib + 1) * args.ldc + j] = h1;
-                        C[static_cast<int64_t>(ib + 2) * args.ldc + j] = h2;
-                        C[static_cast<int64_t>(ib + 3) * args.ldc + j] = h3;
-                        u32x2 pk;
-                        pk.x = pack2(h0, h1);
-                        pk.y = pack2(h2, h3);
-                        *reinterpret_cast<u32x2*>(C + static_cast<int64_t>(j) * args.ldc + ib) = pk;
-                    } else {
-                        const bf16_t hv[4] = {h0, h1, h2, h3};
+    // every wave is done with the K loop's LDS stages before any reuses them
+    __syncthreads();
+    bf16_t* W = lds + wave * (WTM * WTN);
+    constexpr int CT_ = WTM / 8;  // 16-byte chunks per row of the transposed sub-tile (WTN rows)
+    constexpr int CN_ = WTN / 8;  // and of the direct one (WTM rows)
+
+    // (a) write the transposed sub-tile [jj][ii]: 8-byte pieces, chunk index
+    // XOR-swizzled with the row so the 32 rows a store touches spread over
+    // the banks
+    auto put_t = [&]() {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            if (ib + q <= j) {
-                                C[static_cast<int64_t>(ib + q) * args.ldc + j] = hv[q];
-                                C[static_cast<int64_t>(j) * args.ldc + ib + q] = hv[q];
-                            }
-                        }
-                    }
-                } else if constexpr (KIND == GEMM_BX) {
-                    bf16_t* C = args.C + cm * args.c_mat;
-                    bf16_t* CT = args.CT + cm * args.ct_mat;
-                    C[static_cast<int64_t>(ib + 0) * args.ldc + j] = h0;
-                    C[static_cast<int64_t>(ib + 1) * args.ldc + j] = h1;
-                    C[static_cast<int64_t>(ib + 2) * args.ldc + j] = h2;
-                    C[static_cast<int64_t>(ib + 3) * args.ldc + j] = h3;
-                    u32x2 pk;
-                    pk.x = pack2(h0, h1);
-                    pk.y = pack2(h2, h3);
-                    *reinterpret_cast<u32x2*>(CT + static_cast<int64_t>(j) * args.ldct + ib) = pk;
-                } else {  // GEMM_BX_FINAL: float32 output in G's orientation
-                    float* o = out.p[mat];
-                    if (j < args.n) {
-                        const float f[4] = {bf16_to_f32(h0), bf16_to_f32(h1), bf16_to_f32(h2), bf16_to_f32(h3)};
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int i = ib + q;
-                            if (i < args.m) {
-                                if (args.tall)
-                                    o[static_cast<int64_t>(j) * args.m + i] = f[q];
-                                else
-                                    o[static_cast<int64_t>(i) * args.n + j] = f[q];
-                            }
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int jj = fn * 32 + (lane & 31);
+                    const int ii = fm * 32 + 8 * g4 + 4 * (lane >> 5);
+                    *reinterpret_cast<u32x2*>(W + jj * WTM + (((ii >> 3) ^ (jj & (CT_ - 1))) << 3) + (ii & 7)) =
+                        hv[fm][fn][g4];
+                }
+    };
+    // (b) write the direct sub-tile [ii][jj] (2-byte pieces); `sym` keeps
+    // only ii <= jj and mirrors it, which makes a diagonal sub-tile exactly
+    // symmetric
+    auto put_n = [&](bool sym) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int jj = fn * 32 + (lane & 31);
+                    const int ib = fm * 32 + 8 * g4 + 4 * (lane >> 5);
+                    const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int ii = ib + q;
+                        const bf16_t h = static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+                        if (!sym || ii <= jj) {
+                            W[ii * WTN + (((jj >> 3) ^ (ii & (CN_ - 1))) << 3) + (jj & 7)] = h;
+                            if (sym) W[jj * WTN + (((ii >> 3) ^ (jj & (CN_ - 1))) << 3) + (ii & 7)] = h;
                         }
                     }
                 }
+    };
+    auto lds_fence = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    // (c) store the LDS sub-tile (ROWS rows of CPR chunks) as bf16 rows of
+    // dst with leading dimension ld
+    auto store_bf16 = [&](int rows, int cpr, bf16_t* dst, int ld) {
+        for (int q = lane; q < rows * cpr; q += 64) {
+            const int row = q / cpr, c = q % cpr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (row & (cpr - 1))) << 3));
+            *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(row) * ld + c * 8) = v;
+        }
+    };
+
+    if constexpr (SYM) {
+        bf16_t* C = args.C + cm * args.c_mat;
+        if (ti != tj || wm < wn) {
+            // off-diagonal block: the block itself and its mirror
+            put_t();
+            lds_fence();
+            store_bf16(WTN, CT_, C + static_cast<int64_t>(j0w) * args.ldc + i0w, args.ldc);
+            lds_fence();
+            put_n(false);
+            lds_fence();
+            store_bf16(WTM, CN_, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+        } else if (wm == wn) {
+            // diagonal block: symmetrised once, stored once
+            put_n(true);
+            lds_fence();
+            store_bf16(WTM, CN_, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+        }
+        // (wm > wn on a diagonal tile: the mirror of the wm < wn block)
+    } else if constexpr (KIND == GEMM_BX) {
+        put_t();
+        lds_fence();
+        store_bf16(WTN, CT_, args.CT + cm * args.ct_mat + static_cast<int64_t>(j0w) * args.ldct + i0w, args.ldct);
+        lds_fence();
+        put_n(false);
+        lds_fence();
+        store_bf16(WTM, CN_, args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+    } else {  // GEMM_BX_FINAL: float32 output in G's orientation, clipped to m x n
+        float* o = out.p[args.out_base + mat];
+        const bool tall = args.tall != 0;
+        const int rows = tall ? WTN : WTM, cpr = tall ? CT_ : CN_;
+        const int r0 = tall ? j0w : i0w, c0 = tall ? i0w : j0w;   // origin in the output
+        const int rlim = tall ? args.n : args.m, clim = tall ? args.m : args.n;  // output rows x cols
+        if (tall) put_t(); else put_n(false);
+        lds_fence();
+        const bool vec_ok = (clim & 3) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
+        for (int q = lane; q < rows * cpr; q += 64) {
+            const int row = q / cpr, c = q % cpr;
+            const int gr = r0 + row, gc = c0 + c * 8;
+            if (gr >= rlim || gc >= clim) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (row & (cpr - 1))) << 3));
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = bf16_to_f32(static_cast<bf16_t>(v[e] & 0xffffu));
+                f[2 * e + 1] = bf16_to_f32(static_cast<bf16_t>(v[e] >> 16));
+            }
+            float* dst = o + static_cast<int64_t>(gr) * clim + gc;
+            if (vec_ok && gc + 8 <= clim) {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{f[0], f[1], f[2], f[3]};
+                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{f[4], f[5], f[6], f[7]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gc + e < clim) dst[e] = f[e];
             }
         }
     }
 }
 
 template <int BM, int BN, int BK, int STAGES>
-hipError_t launch_t(GemmKind kind, const GemmArgs& args, int cnt, const PtrTable* out, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(args.tiles_per_mat) * cnt);
+hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTable* out, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(blocks));
     PtrTable o{};
     if (out) o = *out;
     switch (kind) {
-        case GEMM_SYRK: k_gemm_nt<BM, BM, BK, STAGES, GEMM_SYRK><<<grid, kThreads, 0, stream>>>(args, o); break;
-        case GEMM_AAB: k_gemm_nt<BM, BM, BK, STAGES, GEMM_AAB><<<grid, kThreads, 0, stream>>>(args, o); break;
-        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX><<<grid, kThreads, 0, stream>>>(args, o); break;
+        case GEMM_SYRK: k_gemm_nt<BM, BM, BK, STAGES, GEMM_SYRK><<<grid, kThreads, 0, stream>>>(L, o); break;
+        case GEMM_AAB: k_gemm_nt<BM, BM, BK, STAGES, GEMM_AAB><<<grid, kThreads, 0, stream>>>(L, o); break;
+        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX><<<grid, kThreads, 0, stream>>>(L, o); break;
         case GEMM_BX_FINAL:
-            k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX_FINAL><<<grid, kThreads, 0, stream>>>(args, o);
+            k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX_FINAL><<<grid, kThreads, 0, stream>>>(L, o);
             break;
     }
     return hipGetLastError();
@@ -361,25 +440,22 @@ hipError_t launch_t(GemmKind kind, const GemmArgs& args, int cnt, const PtrTable
 
 }  // namespace
 
-hipError_t launch_gemm(GemmKind kind, int tile, const GemmArgs& args, int cnt, const PtrTable* out,
+hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
                        hipStream_t stream) {
-    // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages,
-    // 2 = BK 32 with 3 stages (MUON_GEMM_PIPE in the environment, for tuning)
+    // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages
+    // (MUON_GEMM_PIPE in the environment, for tuning)
     static const int pipe = [] {
         const char* s = getenv("MUON_GEMM_PIPE");
         const int v = s ? atoi(s) : 0;
-        return (v >= 0 && v <= 2) ? v : 0;
+        return (v >= 0 && v <= 1) ? v : 0;
     }();
     switch (tile * 4 + pipe) {
-        case 64 * 4 + 0: return launch_t<64, 64, 64, 2>(kind, args, cnt, out, stream);
-        case 64 * 4 + 1: return launch_t<64, 64, 32, 4>(kind, args, cnt, out, stream);
-        case 64 * 4 + 2: return launch_t<64, 64, 32, 3>(kind, args, cnt, out, stream);
-        case 128 * 4 + 0: return launch_t<128, 128, 64, 2>(kind, args, cnt, out, stream);
-        case 128 * 4 + 1: return launch_t<128, 128, 32, 4>(kind, args, cnt, out, stream);
-        case 128 * 4 + 2: return launch_t<128, 128, 32, 3>(kind, args, cnt, out, stream);
-        case 256 * 4 + 0: return launch_t<256, 256, 64, 2>(kind, args, cnt, out, stream);
-        case 256 * 4 + 1: return launch_t<256, 256, 32, 4>(kind, args, cnt, out, stream);
-        case 256 * 4 + 2: return launch_t<256, 256, 32, 3>(kind, args, cnt, out, stream);
+        case 64 * 4 + 0: return launch_t<64, 64, 64, 2>(kind, launch, blocks, out, stream);
+        case 64 * 4 + 1: return launch_t<64, 64, 32, 4>(kind, launch, blocks, out, stream);
+        case 128 * 4 + 0: return launch_t<128, 128, 64, 2>(kind, launch, blocks, out, stream);
+        case 128 * 4 + 1: return launch_t<128, 128, 32, 4>(kind, launch, blocks, out, stream);
+        case 256 * 4 + 0: return launch_t<256, 256, 64, 2>(kind, launch, blocks, out, stream);
+        case 256 * 4 + 1: return launch_t<256, 256, 32, 4>(kind, launch, blocks, out, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -46,7 +46,15 @@ bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* plan);
 
 enum GemmKind { GEMM_SYRK = 0, GEMM_AAB = 1, GEMM_BX = 2, GEMM_BX_FINAL = 3 };
 
+// One segment of a GEMM launch: `cnt` same-shaped matrices laid out as in
+// an Ns5Plan.  A launch covers up to kMaxSeg segments that share the tile
+// size; workgroups [first_block, first_block + cnt * tiles_per_mat) of the
+// launch's logical grid belong to this segment.
+constexpr int kMaxSeg = 8;
+
 struct GemmArgs {
+    int first_block;
+    int out_base;       // index of the segment's first matrix in the output table
     const bf16_t* P;
     int64_t p_mat;
     int ldp;
@@ -70,6 +78,11 @@ struct GemmArgs {
     int m, n, tall;
 };
 
+struct GemmLaunch {
+    GemmArgs seg[kMaxSeg];
+    int nseg;
+};
+
 hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, float mu,
                            hipStream_t stream);
 
@@ -82,7 +95,7 @@ hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& pla
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
                            hipStream_t stream);
 
-hipError_t launch_gemm(GemmKind kind, int tile, const GemmArgs& args, int cnt, const PtrTable* out,
+hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
                        hipStream_t stream);
 
 }  // namespace muon

@@ -26,7 +26,8 @@ MAX_GROUP = 128
 
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
-           "muon_ns5_grouped_timed", "muon_status_string", "muon_last_error")
+           "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_ns5_batched_timed",
+           "muon_status_string", "muon_last_error")
 
 
 class MuonError(RuntimeError):
@@ -49,10 +50,16 @@ def _load():
     lib.muon_ns5_grouped.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
                                      ctypes.c_float, vp, sz, vp]
     lib.muon_ns5_grouped.restype = ctypes.c_int
-    lib.muon_ns5_grouped_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
+    pi64 = ctypes.POINTER(i64)
+    lib.muon_ns5_batched_workspace_size.argtypes = [pi64, pi64, i64]
+    lib.muon_ns5_batched_workspace_size.restype = sz
+    lib.muon_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
+                                     ctypes.c_float, vp, sz, vp]
+    lib.muon_ns5_batched.restype = ctypes.c_int
+    lib.muon_ns5_batched_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
                                            ctypes.c_float, vp, sz, vp, ctypes.POINTER(vp), ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_int)]
-    lib.muon_ns5_grouped_timed.restype = ctypes.c_int
+    lib.muon_ns5_batched_timed.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
@@ -142,14 +149,9 @@ def ns5(G, out=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
     return out
 
 
-def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None):
+def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
     """NS5 of a list of same-shaped float32 matrices, batched per launch.
-    Returns the list of outputs (new tensors unless given).
-
-    ``events`` (measurement): a list of ``torch.cuda.Event(enable_timing=True)``
-    pairs ``[start0, stop0, start1, stop1, ...]``; the library records them
-    around the a X + B X launches of the non-final steps.  The number of
-    pairs recorded is then available as ``ns5_grouped.last_recorded``."""
+    Returns the list of outputs (new tensors unless given)."""
     Gs = list(Gs)
     if not Gs:
         return []
@@ -158,15 +160,7 @@ def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
     shape, device = Gs[0].shape, Gs[0].device
     if len(shape) != 2 or any(G.shape != shape or G.device != device for G in Gs):
         raise ValueError("all matrices must be 2-D with the same shape and device")
-    if outs is None:
-        outs = [torch.empty_like(G) for G in Gs]
-    outs = list(outs)
-    if len(outs) != len(Gs):
-        raise ValueError("outs must match Gs in length")
-    for i, o in enumerate(outs):
-        _require_f32_cuda(o, f"outs[{i}]")
-        if o.shape != shape or o.device != device:
-            raise ValueError("every output must have the inputs' shape and device")
+    outs = _outputs(Gs, outs)
     rows, cols = shape
     count = len(Gs)
     need = workspace_size(rows, cols, count)
@@ -176,18 +170,74 @@ def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
     ws = workspace if workspace is not None else _workspace(device, stream, need)
     g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
     o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    _check(lib.muon_ns5_grouped(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps), ws.data_ptr(),
+                                ws.numel() * ws.element_size(), stream))
+    return outs
+
+
+def _outputs(Gs, outs):
+    if outs is None:
+        return [torch.empty_like(G) for G in Gs]
+    outs = list(outs)
+    if len(outs) != len(Gs):
+        raise ValueError("outs must match Gs in length")
+    for i, (G, o) in enumerate(zip(Gs, outs)):
+        _require_f32_cuda(o, f"outs[{i}]")
+        if o.shape != G.shape or o.device != G.device:
+            raise ValueError(f"outs[{i}] must have the shape and device of Gs[{i}]")
+    return outs
+
+
+def batched_workspace_size(shapes):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * n)(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * n)(*[int(s[1]) for s in shapes])
+    return int(lib.muon_ns5_batched_workspace_size(rows, cols, n))
+
+
+def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None):
+    """NS5 of a list of float32 matrices of any shapes (one device), with one
+    launch per product and NS5 step over all matrices that share a tile size.
+    Returns the list of outputs (new tensors unless given).
+
+    ``events`` (measurement): a list of ``torch.cuda.Event(enable_timing=True)``
+    pairs ``[start0, stop0, start1, stop1, ...]``; the library records them
+    around the a X + B X launches of the non-final steps.  The number of
+    pairs recorded is then available as ``ns5_batched.last_recorded``."""
+    Gs = list(Gs)
+    if not Gs:
+        return []
+    for i, G in enumerate(Gs):
+        _require_f32_cuda(G, f"Gs[{i}]")
+        if G.dim() != 2:
+            raise ValueError(f"Gs[{i}] must be 2-D")
+    device = Gs[0].device
+    if any(G.device != device for G in Gs):
+        raise ValueError("all matrices must be on one device")
+    outs = _outputs(Gs, outs)
+    count = len(Gs)
+    shapes = [tuple(G.shape) for G in Gs]
+    need = batched_workspace_size(shapes)
+    if need == 0:
+        raise MuonError(MUON_ERR_UNSUPPORTED, "a shape is not supported")
+    stream = _stream_handle(device)
+    ws = workspace if workspace is not None else _workspace(device, stream, need)
+    rows = (ctypes.c_int64 * count)(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * count)(*[s[1] for s in shapes])
+    g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
+    o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    nbytes = ws.numel() * ws.element_size()
     if events is None:
-        _check(lib.muon_ns5_grouped(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps), ws.data_ptr(),
-                                    ws.numel() * ws.element_size(), stream))
+        _check(lib.muon_ns5_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps), ws.data_ptr(),
+                                    nbytes, stream))
     else:
         if len(events) % 2:
             raise ValueError("events must come in (start, stop) pairs")
         ev = (ctypes.c_void_p * max(len(events), 1))(*[e.cuda_event for e in events])
         rec = ctypes.c_int(0)
-        _check(lib.muon_ns5_grouped_timed(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps),
-                                          ws.data_ptr(), ws.numel() * ws.element_size(), stream, ev,
-                                          len(events) // 2, ctypes.byref(rec)))
-        ns5_grouped.last_recorded = rec.value
+        _check(lib.muon_ns5_batched_timed(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps),
+                                          ws.data_ptr(), nbytes, stream, ev, len(events) // 2, ctypes.byref(rec)))
+        ns5_batched.last_recorded = rec.value
     return outs
 
 

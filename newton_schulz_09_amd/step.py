@@ -5,8 +5,8 @@ the Muon section's summary paragraph, Synced report on Modded-NanoGPT).
 Memory is laid out for one GPU's HBM: the gradients, momentum buffers,
 momentum outputs and orthogonalised updates are four flat float32 buffers
 with a view per matrix, so momentum is a single streaming launch over all
-parameters, and NS5 runs as one grouped call per distinct shape, sharing one
-workspace (the calls are ordered on one stream).
+parameters, and NS5 is one batched call over all matrices (each product of
+each NS5 step is a single launch over every matrix that shares a tile size).
 """
 
 import torch
@@ -39,7 +39,7 @@ class MuonStep:
         self.groups = {}
         for i, s in enumerate(self.shapes):
             self.groups.setdefault(s, []).append(i)
-        need = max(muon.workspace_size(r, c, len(ix)) for (r, c), ix in self.groups.items())
+        need = muon.batched_workspace_size(self.shapes)
         if need == 0:
             raise muon.MuonError(muon.MUON_ERR_UNSUPPORTED, "a shape is beyond the supported limits")
         self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
@@ -50,10 +50,16 @@ class MuonStep:
     def momentum(self):
         muon.momentum_nesterov(self.grad, self.buf, self.u, self.mu)
 
-    def orthogonalise(self):
-        for ix in self.groups.values():
-            muon.ns5_grouped([self.us[i] for i in ix], [self.outs[i] for i in ix], steps=self.steps,
-                             eps=self.eps, workspace=self.workspace)
+    def orthogonalise(self, events=None):
+        """NS5 of every momentum output in one batched call: each product of
+        each NS5 step is one launch over all matrices (``events``: see
+        ``muon.ns5_batched``)."""
+        muon.ns5_batched(self.us, self.outs, steps=self.steps, eps=self.eps, workspace=self.workspace,
+                         events=events)
+
+    def last_recorded(self):
+        """Event pairs recorded by the last ``orthogonalise(events=...)``."""
+        return muon.ns5_batched.last_recorded
 
     def step(self):
         """Enqueue one step on the current stream; results land in ``outs``

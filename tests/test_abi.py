@@ -96,3 +96,48 @@ def test_binding_rejects_cpu_tensors(muon):
         muon.momentum_nesterov(g, g.clone())
     with pytest.raises(ValueError):
         muon.ns5(torch.zeros(4, 4))
+
+
+def test_batched_workspace_size(muon):
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768)] * 12
+    s = muon.batched_workspace_size(shapes)
+    # the four shape classes share one pass: at least the sum of their grouped needs
+    assert s >= sum(muon.workspace_size(r, c, 12) for r, c in shapes[:4]) - 4 * 256
+    assert muon.batched_workspace_size([(64, 128)]) == muon.workspace_size(64, 128, 1)
+    assert muon.batched_workspace_size([(0, 5)]) == 0
+    assert muon.batched_workspace_size([(64, 128), (20000, 20000)]) == 0
+    i64 = ctypes.c_int64
+    assert muon.lib.muon_ns5_batched_workspace_size(None, None, 1) == 0
+    assert muon.lib.muon_ns5_batched_workspace_size((i64 * 1)(4), (i64 * 1)(4), 0) == 0
+
+
+def test_batched_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    fake = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_ns5_batched_workspace_size(rows, cols, 2)
+    assert need > 0
+    assert lib.muon_ns5_batched(None, o, rows, cols, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_batched(g, o, None, cols, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_batched(g, o, rows, cols, 0, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_batched(g, o, rows, cols, 2, -1, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    bad = (i64 * 2)(64, 0)
+    assert lib.muon_ns5_batched(g, o, bad, cols, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"matrix 1" in lib.muon_last_error()
+    nullo = (ctypes.c_void_p * 2)(0x300000, 0)
+    assert lib.muon_ns5_batched(g, nullo, rows, cols, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_batched(g, o, rows, cols, 2, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5_batched(g, o, rows, cols, 2, 5, 1e-7, None, need, None) == muon.MUON_ERR_WORKSPACE
+    huge = (i64 * 2)(64, 1 << 15)
+    assert lib.muon_ns5_batched(g, o, huge, (i64 * 2)(128, 1 << 15), 2, 5, 1e-7, ws, 1 << 40, None) \
+        == muon.MUON_ERR_UNSUPPORTED
+    ev = (ctypes.c_void_p * 1)()
+    rec = ctypes.c_int(7)
+    assert lib.muon_ns5_batched_timed(g, o, rows, cols, 2, 5, 1e-7, ws, need, None, None, 1,
+                                      ctypes.byref(rec)) == muon.MUON_ERR_INVALID_ARG
+    assert rec.value == 0
+    del fake, ev

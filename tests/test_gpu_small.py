@@ -175,3 +175,51 @@ def test_diagonal_input(muon):
     off[np.arange(6), np.arange(6)] = 0
     assert not off.any()
     assert np.max(parity.bf16_ulp_diff(out, want)) <= 1
+
+
+# ---------------------------------------------------------------- batched (mixed shapes)
+
+def _bitwise_equal_to_single(muon, Gs, outs):
+    for k, (G, o) in enumerate(zip(Gs, outs)):
+        single = parity.to_np(muon.ns5(G))
+        got = parity.to_np(o)
+        assert np.array_equal(got, single), f"matrix {k} {tuple(G.shape)} differs from the single call"
+
+
+def test_batched_mixed_shapes_equal_single_calls(muon):
+    """Every matrix of a mixed-shape batch gets exactly what muon_ns5 gives it
+    alone (same tile, same kernels, independent matrices)."""
+    shapes = [(64, 128), (128, 64), (65, 130), (130, 65), (3, 5), (768, 300), (300, 768), (64, 128),
+              (200, 520), (200, 520), (1, 1), (96, 4000)]
+    rng = np.random.default_rng(123)
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = muon.ns5_batched(Gs)
+    _bitwise_equal_to_single(muon, Gs, outs)
+    for k in (2, 6, 11):
+        parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(host[k]), f"batched {shapes[k]}")
+
+
+def test_batched_many_shapes_and_passes(muon):
+    """More than 8 distinct shapes and more than 128 matrices: the batch runs
+    in several launch groups and passes over one workspace."""
+    rng = np.random.default_rng(7)
+    shapes = [(40 + 3 * i, 90 + 5 * i) for i in range(11)] * 13 + [(257, 90)] * 3
+    Gs = [cuda(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    outs = muon.ns5_batched(Gs)
+    assert len(outs) == len(shapes) > 128
+    _bitwise_equal_to_single(muon, Gs[:11] + Gs[-4:], outs[:11] + outs[-4:])
+    _bitwise_equal_to_single(muon, Gs[100:104], outs[100:104])
+
+
+def test_batched_zero_steps_and_aliasing(muon):
+    rng = np.random.default_rng(11)
+    host = [rng.standard_normal(s).astype(np.float32) for s in [(70, 90), (90, 70), (33, 33)]]
+    Gs = [cuda(h) for h in host]
+    x0 = muon.ns5_batched(Gs, steps=0)
+    for h, o in zip(host, x0):
+        d = parity.bf16_ulp_diff(parity.to_np(o), oracle.ns5(h, steps=0))
+        assert d.max() <= 1 and np.mean(d == 0) >= 0.999
+    muon.ns5_batched(Gs, outs=Gs)            # in place
+    for h, g in zip(host, Gs):
+        parity.assert_ns5_parity(parity.to_np(g), oracle.ns5(h), "batched in place")
