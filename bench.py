@@ -55,6 +55,36 @@ def parse():
 
 COPY_BYTES = 1 << 30
 
+# HBM-side traffic of the dominant kernel per launch, from two rocprofv3 --pmc
+# runs over `bench.py --steps 2 --warmup 1 --skip-extras` (FETCH_SIZE, then
+# WRITE_SIZE, in KiB per dispatch), scaled by what the same counters read for
+# the 1 GiB copy of `bench.py --copy-calibration` (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0).  Valid only for the kernel sources it was measured with:
+# reported as null once their hash differs (the summary is
+# profiles/gpt2_124m_step_traffic.md).
+TRAFFIC = {
+    "sources_sha256": None,
+    "fetch_bytes": None,
+    "write_bytes": None,
+}
+TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
+                   "newton_schulz_09_amd/csrc/internal.hpp", "newton_schulz_09_amd/csrc/common.hpp")
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    if TRAFFIC["sources_sha256"] is None or TRAFFIC["sources_sha256"] != sources_hash():
+        return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
 
 def copy_calibration(torch):
     """A plain copy of a known size: 1 GiB read + 1 GiB written per launch."""
@@ -118,7 +148,7 @@ def time_dominant_kernel(st, steps, torch):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(),
         "launches": launches,
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "flops_per_launch": flops_per_launch,
