@@ -70,6 +70,20 @@ int ld_skew() {
     return skew;
 }
 
+// Tile rows per band of the full-grid product: all of them when there are
+// at most 8 (each column panel of X^T is then read once), else 4
+// (MUON_GEMM_BAND=n caps it at n, for tuning).
+int band_rows(int tiles_m) {
+    static const int cap = [] {
+        const char* s = getenv("MUON_GEMM_BAND");
+        const int v = s ? atoi(s) : 0;
+        return v >= 1 ? v : 0;
+    }();
+    int b = tiles_m <= 8 ? tiles_m : 4;
+    if (cap && b > cap) b = cap;
+    return b;
+}
+
 // A dispatch's grid (workgroups x 256 work-items) must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t{1} << 32) / kThreads - 1;
 
@@ -307,6 +321,7 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
                 g3.Q = b.XT[cur]; g3.q_mat = xte; g3.ldq = pl.ldxt;
                 g3.kpad = static_cast<int>(round_up(pl.m, 64));
                 g3.tiles = tiles_m; g3.tiles_n = tiles_n; g3.tiles_per_mat = tiles_m * tiles_n;
+                g3.band = band_rows(tiles_m);
                 g3.E = b.XT[cur]; g3.e_mat = xte; g3.lde = pl.ldxt;
                 g3.alpha = MUON_NS5_A; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;

@@ -28,12 +28,19 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16, round to nearest, ties to even: gfx950's
+// v_cvt_pk_bf16_f32 (NaN comes out quiet).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two float32 -> two bfloat16 (same rounding) packed as lo | hi << 16, one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // float64 -> bfloat16 with a single rounding (nearest, ties to even) for the

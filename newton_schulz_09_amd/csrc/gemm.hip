@@ -35,8 +35,10 @@
 // tile size) in the same launch.  Consecutive workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so the workgroup index is remapped to
 // give every XCD a contiguous range of tiles; within a matrix, tiles of the
-// full grid are ordered in bands of kBand tile rows (column by column inside
-// a band), so that the tiles resident on one XCD share operand panels.
+// full grid are ordered in bands of `band` tile rows, column by column inside
+// a band, so that the tiles resident on one XCD share operand panels (with
+// all tile rows in one band, each column panel of the second operand is read
+// from memory once).
 #include <stdlib.h>
 
 #include "internal.hpp"
@@ -46,7 +48,6 @@ namespace muon {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kBand = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -60,10 +61,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ int xcd_remap(int b, int G) {
     const int q = G / kXcds, r = G % kXcds, x = b % kXcds;
     return x * q + (x < r ? x : r) + b / kXcds;
-}
-
-__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
-    return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
 
 // Slot permutation of row r for CPR 16-byte chunks per row (8 or 4).
@@ -122,17 +119,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
         }
         tj = ti + t;
     } else {
-        const int per_band = kBand * args.tiles_n;
+        const int per_band = args.band * args.tiles_n;
         const int band = t / per_band;
-        const int first = band * kBand;
-        const int rows_in_band = args.tiles - first < kBand ? args.tiles - first : kBand;
+        const int first = band * args.band;
+        const int rows_in_band = args.tiles - first < args.band ? args.tiles - first : args.band;
         const int w = t - band * per_band;
         ti = first + w % rows_in_band;
         tj = w / rows_in_band;
     }
     const int i0 = ti * BM, j0 = tj * BN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
     const int wm = wave >> 1, wn = wave & 1;
 
     // ---- loader: load i of this wave fills rows r0 = (wave*IP + i)*RPI ..
@@ -186,6 +184,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+
+    // The epilogue's second operand (AAB: A[j][i]; BX: old X[i][j] = X^T[j][i])
+    // is the K slice [i0, i0 + BM) of the Q operand, which passes through LDS
+    // during the K loop: for tiles up to 128 each wave copies its values out of
+    // the stage of the matching K step, so they are never read from memory
+    // again.  K steps past kpad hold only padding, whose values are zero.
+    constexpr bool CAPTURE_E =
+        (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) && BM <= 128;
+    u32x2 ev[CAPTURE_E ? FM : 1][CAPTURE_E ? FN : 1][4];
+    if constexpr (CAPTURE_E) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) ev[fm][fn][g4] = u32x2{0u, 0u};
+    }
 
     const int nk = args.kpad / BK;
     // Every iteration issues the NLOAD loads of one K step (STAGES-1 steps
@@ -255,6 +270,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CAPTURE_E) {
+            const bf16_t* sQs = lds + (kt % STAGES) * STAGE + BM * BK;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int ik = i0 + wm * WTM + fm * 32;  // first K index of this fragment row block
+                if (kt == ik / BK) {
+                    const int kin = ik - kt * BK;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const int jrow = wn * WTN + fn * 32 + (lane & 31);
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int kk = kin + 8 * g4 + 4 * (lane >> 5);
+                            ev[fm][fn][g4] = *reinterpret_cast<const u32x2*>(
+                                sQs + jrow * BK + (((kk >> 3) ^ swz<CPR>(jrow)) << 3) + (kk & 7));
+                        }
+                    }
+                }
+            }
+        }
     }
     // drain the loads of the clamped tail steps before the epilogue
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -282,12 +317,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                 if constexpr (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) {
                     // AAB: A[i][j] = A[j][i] (symmetric); BX: old X[i][j] =
                     // X^T[j][i].  Either way a contiguous run of 4 along i.
-                    const u32x2 ev = *reinterpret_cast<const u32x2*>(
-                        args.E + cm * args.e_mat + static_cast<int64_t>(j) * args.lde + ib);
-                    const float e0 = bf16_to_f32(static_cast<bf16_t>(ev.x & 0xffffu));
-                    const float e1 = bf16_to_f32(static_cast<bf16_t>(ev.x >> 16));
-                    const float e2 = bf16_to_f32(static_cast<bf16_t>(ev.y & 0xffffu));
-                    const float e3 = bf16_to_f32(static_cast<bf16_t>(ev.y >> 16));
+                    u32x2 e4;
+                    if constexpr (CAPTURE_E)
+                        e4 = ev[fm][fn][g4];
+                    else
+                        e4 = *reinterpret_cast<const u32x2*>(args.E + cm * args.e_mat +
+                                                             static_cast<int64_t>(j) * args.lde + ib);
+                    const float e0 = bf16_to_f32(static_cast<bf16_t>(e4.x & 0xffffu));
+                    const float e1 = bf16_to_f32(static_cast<bf16_t>(e4.x >> 16));
+                    const float e2 = bf16_to_f32(static_cast<bf16_t>(e4.y & 0xffffu));
+                    const float e3 = bf16_to_f32(static_cast<bf16_t>(e4.y >> 16));
                     if constexpr (KIND == GEMM_AAB) {  // b A + c (A A)
                         v0 = fmaf(args.beta, v0, args.alpha * e0);
                         v1 = fmaf(args.beta, v1, args.alpha * e1);
@@ -300,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                         v3 = fmaf(args.alpha, e3, v3);
                     }
                 }
-                hv[fm][fn][g4].x = pack2(f32_to_bf16(v0), f32_to_bf16(v1));
-                hv[fm][fn][g4].y = pack2(f32_to_bf16(v2), f32_to_bf16(v3));
+                hv[fm][fn][g4].x = f32x2_to_bf16x2(v0, v1);
+                hv[fm][fn][g4].y = f32x2_to_bf16x2(v2, v3);
             }
         }
     }
@@ -328,9 +367,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                         hv[fm][fn][g4];
                 }
     };
-    // (b) write the direct sub-tile [ii][jj] (2-byte pieces); `sym` keeps
-    // only ii <= jj and mirrors it, which makes a diagonal sub-tile exactly
-    // symmetric
+    // (b) write the direct sub-tile [ii][jj] (2-byte pieces).  Its chunk
+    // swizzle is keyed on ii / 4, so a lane's run of 4 rows shares one
+    // address computation (the rows are immediate offsets).  `sym` keeps only
+    // ii <= jj and mirrors it, which makes a diagonal sub-tile exactly
+    // symmetric.
     auto put_n = [&](bool sym) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -341,13 +382,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                     const int jj = fn * 32 + (lane & 31);
                     const int ib = fm * 32 + 8 * g4 + 4 * (lane >> 5);
                     const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
+                    bf16_t* row0 = W + ib * WTN + (((jj >> 3) ^ ((ib >> 2) & (CN_ - 1))) << 3) + (jj & 7);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int ii = ib + q;
                         const bf16_t h = static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
                         if (!sym || ii <= jj) {
-                            W[ii * WTN + (((jj >> 3) ^ (ii & (CN_ - 1))) << 3) + (jj & 7)] = h;
-                            if (sym) W[jj * WTN + (((ii >> 3) ^ (jj & (CN_ - 1))) << 3) + (ii & 7)] = h;
+                            row0[q * WTN] = h;
+                            if (sym) W[jj * WTN + (((ii >> 3) ^ ((jj >> 2) & (CN_ - 1))) << 3) + (ii & 7)] = h;
                         }
                     }
                 }
@@ -355,10 +397,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     auto lds_fence = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
     // (c) store the LDS sub-tile (ROWS rows of CPR chunks) as bf16 rows of
     // dst with leading dimension ld
-    auto store_bf16 = [&](int rows, int cpr, bf16_t* dst, int ld) {
+    // (`shift` selects the layout's swizzle key: row (transposed) or row / 4
+    // (direct))
+    auto store_bf16 = [&](int rows, int cpr, int shift, bf16_t* dst, int ld) {
         for (int q = lane; q < rows * cpr; q += 64) {
             const int row = q / cpr, c = q % cpr;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (row & (cpr - 1))) << 3));
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ ((row >> shift) & (cpr - 1))) << 3));
             *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(row) * ld + c * 8) = v;
         }
     };
@@ -369,26 +414,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
             // off-diagonal block: the block itself and its mirror
             put_t();
             lds_fence();
-            store_bf16(WTN, CT_, C + static_cast<int64_t>(j0w) * args.ldc + i0w, args.ldc);
+            store_bf16(WTN, CT_, 0, C + static_cast<int64_t>(j0w) * args.ldc + i0w, args.ldc);
             lds_fence();
             put_n(false);
             lds_fence();
-            store_bf16(WTM, CN_, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+            store_bf16(WTM, CN_, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
         } else if (wm == wn) {
             // diagonal block: symmetrised once, stored once
             put_n(true);
             lds_fence();
-            store_bf16(WTM, CN_, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+            store_bf16(WTM, CN_, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
         }
         // (wm > wn on a diagonal tile: the mirror of the wm < wn block)
     } else if constexpr (KIND == GEMM_BX) {
         put_t();
         lds_fence();
-        store_bf16(WTN, CT_, args.CT + cm * args.ct_mat + static_cast<int64_t>(j0w) * args.ldct + i0w, args.ldct);
+        store_bf16(WTN, CT_, 0, args.CT + cm * args.ct_mat + static_cast<int64_t>(j0w) * args.ldct + i0w, args.ldct);
         lds_fence();
         put_n(false);
         lds_fence();
-        store_bf16(WTM, CN_, args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+        store_bf16(WTM, CN_, 2, args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
     } else {  // GEMM_BX_FINAL: float32 output in G's orientation, clipped to m x n
         float* o = out.p[args.out_base + mat];
         const bool tall = args.tall != 0;
@@ -402,7 +447,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
             const int row = q / cpr, c = q % cpr;
             const int gr = r0 + row, gc = c0 + c * 8;
             if (gr >= rlim || gc >= clim) continue;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (row & (cpr - 1))) << 3));
+            const int key = tall ? row : (row >> 2);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (key & (cpr - 1))) << 3));
             float f[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -442,18 +488,29 @@ hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTab
 
 hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
                        hipStream_t stream) {
-    // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages
-    // (MUON_GEMM_PIPE in the environment, for tuning)
+    // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages,
+    // 2 = BK 32 with 2 stages for tiles up to 128 (half the LDS, so more
+    // workgroups per CU) (MUON_GEMM_PIPE in the environment, for tuning)
     static const int pipe = [] {
         const char* s = getenv("MUON_GEMM_PIPE");
         const int v = s ? atoi(s) : 0;
-        return (v >= 0 && v <= 1) ? v : 0;
+        return (v >= 0 && v <= 4) ? v : 0;
     }();
-    switch (tile * 4 + pipe) {
+    if (pipe >= 3) {
+        switch (tile * 8 + pipe) {
+            case 128 * 8 + 3: return launch_t<128, 128, 64, 3>(kind, launch, blocks, out, stream);
+            case 128 * 8 + 4: return launch_t<128, 128, 64, 4>(kind, launch, blocks, out, stream);
+            default: break;
+        }
+    }
+    switch (tile * 4 + (pipe >= 3 ? 0 : pipe)) {
         case 64 * 4 + 0: return launch_t<64, 64, 64, 2>(kind, launch, blocks, out, stream);
         case 64 * 4 + 1: return launch_t<64, 64, 32, 4>(kind, launch, blocks, out, stream);
         case 128 * 4 + 0: return launch_t<128, 128, 64, 2>(kind, launch, blocks, out, stream);
         case 128 * 4 + 1: return launch_t<128, 128, 32, 4>(kind, launch, blocks, out, stream);
+        case 128 * 4 + 2: return launch_t<128, 128, 32, 2>(kind, launch, blocks, out, stream);
+        case 64 * 4 + 2: return launch_t<64, 64, 32, 2>(kind, launch, blocks, out, stream);
+        case 256 * 4 + 2: return launch_t<256, 256, 64, 2>(kind, launch, blocks, out, stream);
         case 256 * 4 + 0: return launch_t<256, 256, 64, 2>(kind, launch, blocks, out, stream);
         case 256 * 4 + 1: return launch_t<256, 256, 32, 4>(kind, launch, blocks, out, stream);
         default: return hipErrorInvalidValue;

@@ -65,6 +65,7 @@ struct GemmArgs {
     int tiles;          // tiles per side of the output grid (rows)
     int tiles_n;        // tiles along the output columns
     int tiles_per_mat;
+    int band;           // full grid: tiles are ordered in bands of this many tile rows
     bf16_t* C;
     int64_t c_mat;
     int ldc;
