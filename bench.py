@@ -3,10 +3,11 @@
 
 A step is one whole Muon hot-path pass over the GPT-2 124M hidden-matrix set
 (12 layers x 768x2304, 768x768, 768x3072, 3072x768; synthetic rank-16 plus
-noise gradients and N(0, 0.1^2) momentum buffers, seed 1): Nesterov momentum
-over all 48 gradients (one launch over flat buffers), then NS5 of every
-momentum output, grouped by shape (4 grouped calls).  Inputs are resident in
-HBM before the timed region.
+noise gradients and N(0, 0.1^2) momentum buffers, seed 1): one
+muon_momentum_ns5_batched call, i.e. Nesterov momentum on all 48 gradients
+fused with the first pass of the norm, then NS5 of every momentum output with
+one launch per product and NS5 step over all 48 matrices.  Inputs are
+resident in HBM before the timed region.
 
 Printed (one JSON line on stdout):
   value          nominal NS5 flops of the step, sum of 5 (4 m^2 n + 2 m^3),
@@ -15,7 +16,8 @@ Printed (one JSON line on stdout):
   roofline       the dominant kernel (the a X + B X product of NS5 steps 1-4)
                  timed with HIP events around each of its launches, against
                  the bf16 dense MFMA peak
-  momentum       the momentum kernel alone (16 bytes per element) against HBM
+  momentum       the stand-alone momentum kernel (16 bytes per element) against
+                 HBM
   ns5_4096       NS5 of one 4096x4096 matrix (U diag(s) V^T, seed 3)
   cpu_baseline   the CPU oracle on a bounded sample of the same step
 """
@@ -107,7 +109,7 @@ def time_step(st, steps, torch):
     torch.cuda.synchronize()
     start.record()
     for _ in range(steps):
-        st.step()
+        st.fused_step()
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
@@ -125,8 +127,7 @@ def time_dominant_kernel(st, steps, torch):
     torch.cuda.synchronize()
     recorded = []
     for s in range(steps):
-        st.momentum()
-        st.orthogonalise(events=events[s])
+        st.fused_step(events=events[s])
         recorded.append(st.last_recorded())
     torch.cuda.synchronize()
     total_ms, launches = 0.0, 0
@@ -233,7 +234,7 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f} s: {len(items)} matrices, {st.total} floats per buffer")
 
     for _ in range(args.warmup):
-        st.step()
+        st.fused_step()
     torch.cuda.synchronize()
     ms = time_step(st, args.steps, torch)
     flops = st.nominal_ns5_flops()

@@ -155,18 +155,45 @@ int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* ro
                      void* stream);
 
 /*
- * Measurement support: exactly muon_ns5_batched, and in addition records
- * caller-created hipEvent_t pairs on `stream` around the launches of the
- * a X + B X product of the non-final steps (the dominant kernel of the
- * iteration): events[2*i] just before and events[2*i+1] just after the i-th
- * such launch, for i < n_event_pairs.  *recorded (if non-null) receives the
- * number of pairs recorded.  With events == NULL it is muon_ns5_batched.
- * Errors: as muon_ns5_batched, plus MUON_ERR_INVALID_ARG for
- * n_event_pairs < 0 or events == NULL with n_event_pairs > 0.
+ * One whole Muon step over a batch: Nesterov momentum (as
+ * muon_momentum_nesterov, per matrix) followed by NS5 of the momentum
+ * output u (as muon_ns5_batched), with the first pass of the norm fused into
+ * the momentum pass.  u is never stored in float32: the fused pass writes the
+ * new buffer, bf16(u) into the workspace and the norm's partial sums, so the
+ * step reads g and buf once.  The result equals momentum followed by NS5 up
+ * to the summation order of the float64 norm.
+ *  g    : host array of `count` device pointers, float32 rows[i] x cols[i]
+ *         gradients, read only.
+ *  buf  : host array of `count` device pointers, the float32 momentum
+ *         buffers (same shapes), read and overwritten with mu*buf + g.
+ *  out  : host array of `count` device pointers, float32 orthogonalised
+ *         updates; out[i] may alias g[i], must not alias buf[i].
+ *  mu   : momentum coefficient.
+ *  Everything else as muon_ns5_batched; the workspace requirement is
+ *  muon_ns5_batched_workspace_size(rows, cols, count).
+ * Errors: as muon_ns5_batched, plus MUON_ERR_INVALID_ARG for a null buf
+ * array or entry, or out[i] == buf[i].
  */
-int muon_ns5_batched_timed(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
-                           int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events, int n_event_pairs, int* recorded);
+int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* const* out, const int64_t* rows,
+                              const int64_t* cols, int64_t count, float mu, int steps, float eps, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement support: muon_ns5_batched (buf == NULL) or
+ * muon_momentum_ns5_batched (buf != NULL, with coefficient mu), which in
+ * addition records caller-created hipEvent_t pairs on `stream` around the
+ * launches of the a X + B X product of the non-final steps (the dominant
+ * kernel of the iteration): events[2*i] just before and events[2*i+1] just
+ * after the i-th such launch, for i < n_event_pairs.  *recorded (if non-null)
+ * receives the number of pairs recorded.  With events == NULL it is the plain
+ * call.
+ * Errors: as the plain call, plus MUON_ERR_INVALID_ARG for n_event_pairs < 0
+ * or events == NULL with n_event_pairs > 0.
+ */
+int muon_ns5_batched_timed(const float* const* G, float* const* out, float* const* buf, float mu,
+                           const int64_t* rows, const int64_t* cols, int64_t count, int steps, float eps,
+                           void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                           int n_event_pairs, int* recorded);
 
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* muon_status_string(int status);

@@ -143,6 +143,7 @@ struct Segment {
     int64_t rows, cols, count;
     const float* const* G;
     float* const* out;
+    float* const* buf;  // momentum buffers (fused Muon step), or null
 };
 
 // Up to kMaxGroup matrices of one segment, with its workspace layout at byte
@@ -150,6 +151,7 @@ struct Segment {
 struct Chunk {
     const float* const* G;
     float* const* out;
+    float* const* buf;
     Ns5Plan plan;
     size_t base;
 };
@@ -190,6 +192,7 @@ int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups) {
             Chunk c;
             c.G = sg.G ? sg.G + start : nullptr;
             c.out = sg.out ? sg.out + start : nullptr;
+            c.buf = sg.buf ? sg.buf + start : nullptr;
             c.plan = pl;
             c.base = g->bytes;
             g->chunks.push_back(c);
@@ -243,7 +246,7 @@ ChunkBufs bufs_of(char* ws, const Chunk& c) {
 
 // The launch sequence: per chunk the norm and the bf16 cast, then per NS5
 // step one launch per product over every chunk of the group.
-int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws, hipStream_t stream,
+int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps, char* ws, hipStream_t stream,
                EventSink* sink) {
     (void)hipGetLastError();  // start from a clean error state
     for (const Group& grp : groups) {
@@ -263,11 +266,24 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
             ChunkBufs b = bufs_of(ws, c);
             ConstPtrTable gt{};
             for (int i = 0; i < pl.cnt; ++i) gt.p[i] = c.G[i];
-            hipError_t e = launch_sumsq(gt, pl.cnt, pl.rows * pl.cols, pl.nb, b.part, stream);
-            if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
+            // fused Muon step: momentum, norm partials and bf16(u) in one pass;
+            // bf16(u) is staged in X[1], which step 1 overwrites later
+            bf16_t* ub = nullptr;
+            const int64_t ub_mat = static_cast<int64_t>(pl.x_elems);
+            hipError_t e;
+            if (c.buf) {
+                PtrTable bt{};
+                for (int i = 0; i < pl.cnt; ++i) bt.p[i] = c.buf[i];
+                ub = b.X[1];
+                e = launch_momentum_norm(gt, bt, pl.cnt, pl.rows * pl.cols, pl.nb, mu, ub, ub_mat, b.part, stream);
+                if (e != hipSuccess) return hip_fail(e, "momentum + norm launch");
+            } else {
+                e = launch_sumsq(gt, pl.cnt, pl.rows * pl.cols, pl.nb, b.part, stream);
+                if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
+            }
             bf16_t* nat = pl.tall ? b.XT[0] : b.X[0];
             bf16_t* tr = pl.tall ? b.X[0] : b.XT[0];
-            e = launch_scale_cast(gt, pl.cnt, pl, b.part, eps, nat, tr, stream);
+            e = launch_scale_cast(gt, ub, ub_mat, pl.cnt, pl, b.part, eps, nat, tr, stream);
             if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
             if (steps == 0) {
                 PtrTable ot{};
@@ -278,6 +294,20 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
         }
         if (steps == 0) continue;
 
+        // tile of the a X + B X product: the group's, or 256 when every chunk's
+        // padded sizes allow it (MUON_BX_TILE=256, for tuning)
+        int bx_tile = grp.tile;
+        {
+            static const int want = [] {
+                const char* e = getenv("MUON_BX_TILE");
+                return e ? atoi(e) : 0;
+            }();
+            if (want == 256) {
+                bool okay = true;
+                for (const Chunk& c : grp.chunks) okay = okay && c.plan.mp % 256 == 0 && c.plan.np % 256 == 0;
+                if (okay) bx_tile = 256;
+            }
+        }
         int cur = 0;
         for (int s = 0; s < steps; ++s) {
             const int nxt = cur ^ 1;
@@ -290,7 +320,7 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
                 const Ns5Plan& pl = c.plan;
                 ChunkBufs b = bufs_of(ws, c);
                 const int T = pl.tile;
-                const int tiles_m = pl.mp / T, tiles_n = pl.np / T;
+                const int tiles_m = pl.mp / T;
                 const int64_t xe = static_cast<int64_t>(pl.x_elems), xte = static_cast<int64_t>(pl.xt_elems);
                 const int64_t ae = static_cast<int64_t>(pl.a_elems);
                 // A = X X^T
@@ -320,8 +350,9 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
                 g3.P = b.B; g3.p_mat = ae; g3.ldp = pl.lda;
                 g3.Q = b.XT[cur]; g3.q_mat = xte; g3.ldq = pl.ldxt;
                 g3.kpad = static_cast<int>(round_up(pl.m, 64));
-                g3.tiles = tiles_m; g3.tiles_n = tiles_n; g3.tiles_per_mat = tiles_m * tiles_n;
-                g3.band = band_rows(tiles_m);
+                const int btm = pl.mp / bx_tile, btn = pl.np / bx_tile;
+                g3.tiles = btm; g3.tiles_n = btn; g3.tiles_per_mat = btm * btn;
+                g3.band = band_rows(btm);
                 g3.E = b.XT[cur]; g3.e_mat = xte; g3.lde = pl.ldxt;
                 g3.alpha = MUON_NS5_A; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
@@ -338,7 +369,7 @@ int run_groups(const std::vector<Group>& groups, int steps, float eps, char* ws,
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded]), stream);
                 if (e != hipSuccess) return hip_fail(e, "event record");
             }
-            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, grp.tile, bx, nb_bx, last ? &out_all : nullptr, stream);
+            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, bx_tile, bx, nb_bx, last ? &out_all : nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "a X + B X launch");
             if (timed) {
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded + 1]), stream);
@@ -366,14 +397,16 @@ int grouped_segment(const float* const* G, float* const* out, int64_t count, int
     seg->count = count;
     seg->G = G;
     seg->out = out;
+    seg->buf = nullptr;
     return MUON_OK;
 }
 
 // A mixed-shape batch bucketed into segments by shape (in order of first
 // appearance), with per-segment pointer arrays held in `gs` / `os`.
-int batched_segments(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
-                     int64_t count, bool need_ptrs, std::vector<Segment>* segs,
-                     std::vector<std::vector<const float*>>* gs, std::vector<std::vector<float*>>* os) {
+int batched_segments(const float* const* G, float* const* out, float* const* buf, const int64_t* rows,
+                     const int64_t* cols, int64_t count, bool need_ptrs, std::vector<Segment>* segs,
+                     std::vector<std::vector<const float*>>* gs, std::vector<std::vector<float*>>* os,
+                     std::vector<std::vector<float*>>* bs) {
     if (!rows || !cols) return fail(MUON_ERR_INVALID_ARG, "null shape array");
     if (need_ptrs && (!G || !out)) return fail(MUON_ERR_INVALID_ARG, "null pointer array");
     if (count < 1) return fail(MUON_ERR_INVALID_ARG, "count must be >= 1 (got %lld)", (long long)count);
@@ -385,6 +418,10 @@ int batched_segments(const float* const* G, float* const* out, const int64_t* ro
                         (long long)i, (long long)rows[i], (long long)cols[i]);
         if (need_ptrs && (!G[i] || !out[i]))
             return fail(MUON_ERR_INVALID_ARG, "null matrix pointer at index %lld", (long long)i);
+        if (need_ptrs && buf && !buf[i])
+            return fail(MUON_ERR_INVALID_ARG, "null momentum buffer at index %lld", (long long)i);
+        if (need_ptrs && buf && buf[i] == out[i])
+            return fail(MUON_ERR_INVALID_ARG, "out must not alias the momentum buffer (index %lld)", (long long)i);
         int k = 0;
         while (k < static_cast<int>(key_r.size()) && !(key_r[k] == rows[i] && key_c[k] == cols[i])) ++k;
         if (k == static_cast<int>(key_r.size())) {
@@ -396,6 +433,7 @@ int batched_segments(const float* const* G, float* const* out, const int64_t* ro
     const size_t nk = key_r.size();
     gs->assign(nk, {});
     os->assign(nk, {});
+    bs->assign(nk, {});
     std::vector<int64_t> cnt(nk, 0);
     for (int64_t i = 0; i < count; ++i) {
         const int k = which[static_cast<size_t>(i)];
@@ -403,6 +441,7 @@ int batched_segments(const float* const* G, float* const* out, const int64_t* ro
         if (need_ptrs) {
             (*gs)[k].push_back(G[i]);
             (*os)[k].push_back(out[i]);
+            if (buf) (*bs)[k].push_back(buf[i]);
         }
     }
     segs->clear();
@@ -413,27 +452,28 @@ int batched_segments(const float* const* G, float* const* out, const int64_t* ro
         sg.count = cnt[k];
         sg.G = need_ptrs ? (*gs)[k].data() : nullptr;
         sg.out = need_ptrs ? (*os)[k].data() : nullptr;
+        sg.buf = (need_ptrs && buf) ? (*bs)[k].data() : nullptr;
         segs->push_back(sg);
     }
     return MUON_OK;
 }
 
-int run_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
-                int64_t count, int steps, float eps, void* ws, size_t ws_bytes, hipStream_t stream,
-                EventSink* sink) {
+int run_batched(const float* const* G, float* const* out, float* const* buf, float mu, const int64_t* rows,
+                const int64_t* cols, int64_t count, int steps, float eps, void* ws, size_t ws_bytes,
+                hipStream_t stream, EventSink* sink) {
     int st = check_common(steps, eps);
     if (st) return st;
     std::vector<Segment> segs;
     std::vector<std::vector<const float*>> gs;
-    std::vector<std::vector<float*>> os;
-    st = batched_segments(G, out, rows, cols, count, true, &segs, &gs, &os);
+    std::vector<std::vector<float*>> os, bs;
+    st = batched_segments(G, out, buf, rows, cols, count, true, &segs, &gs, &os, &bs);
     if (st) return st;
     std::vector<Group> groups;
     st = plan_groups(segs.data(), static_cast<int>(segs.size()), &groups);
     if (st) return st;
     st = check_workspace(ws, ws_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, steps, eps, static_cast<char*>(ws), stream, sink);
+    return run_groups(groups, mu, steps, eps, static_cast<char*>(ws), stream, sink);
 }
 
 }  // namespace
@@ -457,7 +497,7 @@ int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, 
 size_t muon_ns5_workspace_size(int64_t rows, int64_t cols, int64_t count) {
     using namespace muon;
     if (rows < 1 || cols < 1 || count < 1) return 0;
-    Segment sg{rows, cols, count, nullptr, nullptr};
+    Segment sg{rows, cols, count, nullptr, nullptr, nullptr};
     std::vector<Group> groups;
     const std::string saved = g_last_error;
     const int st = plan_groups(&sg, 1, &groups);
@@ -470,9 +510,9 @@ size_t muon_ns5_batched_workspace_size(const int64_t* rows, const int64_t* cols,
     const std::string saved = g_last_error;
     std::vector<Segment> segs;
     std::vector<std::vector<const float*>> gs;
-    std::vector<std::vector<float*>> os;
+    std::vector<std::vector<float*>> os, bs;
     std::vector<Group> groups;
-    int st = batched_segments(nullptr, nullptr, rows, cols, count, false, &segs, &gs, &os);
+    int st = batched_segments(nullptr, nullptr, nullptr, rows, cols, count, false, &segs, &gs, &os, &bs);
     if (!st) st = plan_groups(segs.data(), static_cast<int>(segs.size()), &groups);
     g_last_error = saved;
     return st ? 0 : groups_bytes(groups);
@@ -498,19 +538,30 @@ int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, in
     if (st) return st;
     st = check_workspace(workspace, workspace_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, steps, eps, static_cast<char*>(workspace), static_cast<hipStream_t>(stream), nullptr);
+    return run_groups(groups, 0.0f, steps, eps, static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
+                      nullptr);
 }
 
 int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
                      int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes, void* stream) {
     using namespace muon;
-    return run_batched(G, out, rows, cols, count, steps, eps, workspace, workspace_bytes,
+    return run_batched(G, out, nullptr, 0.0f, rows, cols, count, steps, eps, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream), nullptr);
 }
 
-int muon_ns5_batched_timed(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
-                           int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events, int n_event_pairs, int* recorded) {
+int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* const* out, const int64_t* rows,
+                              const int64_t* cols, int64_t count, float mu, int steps, float eps, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    if (!buf) return fail(MUON_ERR_INVALID_ARG, "null momentum buffer array");
+    return run_batched(g, out, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), nullptr);
+}
+
+int muon_ns5_batched_timed(const float* const* G, float* const* out, float* const* buf, float mu,
+                           const int64_t* rows, const int64_t* cols, int64_t count, int steps, float eps,
+                           void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                           int n_event_pairs, int* recorded) {
     using namespace muon;
     if (recorded) *recorded = 0;
     if (n_event_pairs < 0 || (!events && n_event_pairs > 0))
@@ -518,7 +569,7 @@ int muon_ns5_batched_timed(const float* const* G, float* const* out, const int64
     EventSink sink;
     sink.events = events;
     sink.pairs = events ? n_event_pairs : 0;
-    const int st = run_batched(G, out, rows, cols, count, steps, eps, workspace, workspace_bytes,
+    const int st = run_batched(G, out, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
                                static_cast<hipStream_t>(stream), &sink);
     if (recorded) *recorded = sink.recorded;
     return st;

@@ -90,8 +90,13 @@ hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, 
 hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, double* partials,
                         hipStream_t stream);
 
-hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& plan, const double* partials,
-                             float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream);
+// ub (if non-null): dense bf16 copies of the inputs (stride ub_mat per
+// matrix) to cast from instead of the float32 G.
+hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
+                             const double* partials, float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream);
+
+hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int cnt, int64_t numel, int nb,
+                                float mu, bf16_t* ub, int64_t ub_mat, double* partials, hipStream_t stream);
 
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
                            hipStream_t stream);

@@ -3,7 +3,8 @@
 // Modded-NanoGPT: X = G.bfloat16() / (G.norm() + eps), transposed when G has
 // more rows than columns).
 //
-// Two passes, both HBM-bound:
+// Two passes, both HBM-bound (in the fused Muon step the first is
+// k_momentum_norm, which also applies the momentum and stages bf16(u)):
 //   k_sumsq      reads G once (4 B/elem) and writes one float64 partial sum
 //                of squares per workgroup: per-lane float64 accumulation,
 //                wavefront butterfly shuffles, then LDS across the 4 waves.
@@ -57,16 +58,74 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(ConstPtrTable G, int64_t num
     }
 }
 
+// Nesterov momentum fused with the first pass of the norm: one workgroup per
+// contiguous chunk of one matrix reads g and buf, writes the new buf, writes
+// u rounded to bf16 (the bf16(G) of the cast) into a dense staging copy, and
+// leaves one float64 partial sum of squares of the float32 u.  u itself is
+// never stored in float32.  VEC: 16-byte accesses (pointers 16-byte aligned,
+// numel and chunk multiples of 4).
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_momentum_norm(ConstPtrTable G, PtrTable BUF, int64_t numel, int nb,
+                                                            int64_t chunk, float mu, bf16_t* ub, int64_t ub_mat,
+                                                            double* partials) {
+    const int mat = blockIdx.y;
+    const float* g = G.p[mat];
+    float* buf = BUF.p[mat];
+    bf16_t* u16 = ub + static_cast<int64_t>(mat) * ub_mat;
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t end = begin + chunk < numel ? begin + chunk : numel;
+    double s0 = 0.0, s1 = 0.0;
+    if constexpr (VEC) {
+        for (int64_t i = begin + 4 * static_cast<int64_t>(threadIdx.x); i < end; i += 4 * kThreads) {
+            const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
+            f32x4 bv = *reinterpret_cast<const f32x4*>(buf + i);
+            float u[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bv[q] = fmaf(mu, bv[q], gv[q]);
+                u[q] = fmaf(mu, bv[q], gv[q]);
+            }
+            *reinterpret_cast<f32x4*>(buf + i) = bv;
+            typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2v*>(u16 + i) = u32x2v{f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3])};
+            s0 = fma(static_cast<double>(u[0]), static_cast<double>(u[0]), s0);
+            s1 = fma(static_cast<double>(u[1]), static_cast<double>(u[1]), s1);
+            s0 = fma(static_cast<double>(u[2]), static_cast<double>(u[2]), s0);
+            s1 = fma(static_cast<double>(u[3]), static_cast<double>(u[3]), s1);
+        }
+    } else {
+        for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
+            const float b = fmaf(mu, buf[i], g[i]);
+            const float u = fmaf(mu, b, g[i]);
+            buf[i] = b;
+            u16[i] = f32_to_bf16(u);
+            s0 = fma(static_cast<double>(u), static_cast<double>(u), s0);
+        }
+    }
+    double s = wave_sum(s0 + s1);
+    __shared__ double red[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        partials[static_cast<int64_t>(mat) * nb + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+}
+
 constexpr int kCastTile = 64;
 
-__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int rows, int cols, int tiles_c,
-                                                         const double* partials, int nb, float eps, bf16_t* nat,
-                                                         int ld_nat, int64_t nat_mat, bf16_t* tr, int ld_tr,
-                                                         int64_t tr_mat) {
+// BF16IN: the input is the dense bf16 staging copy written by
+// k_momentum_norm (already bf16(G)); otherwise the float32 G of the table.
+template <bool BF16IN>
+__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const bf16_t* ub, int64_t ub_mat, int rows,
+                                                         int cols, int tiles_c, const double* partials, int nb,
+                                                         float eps, bf16_t* nat, int ld_nat, int64_t nat_mat,
+                                                         bf16_t* tr, int ld_tr, int64_t tr_mat) {
     const int mat = blockIdx.y;
     const int tr_i = blockIdx.x / tiles_c, tc_i = blockIdx.x % tiles_c;
     const int r0 = tr_i * kCastTile, c0 = tc_i * kCastTile;
-    const float* g = G.p[mat];
+    const float* g = BF16IN ? nullptr : G.p[mat];
+    const bf16_t* u16 = BF16IN ? ub + static_cast<int64_t>(mat) * ub_mat : nullptr;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     __shared__ double s_norm;
@@ -89,9 +148,14 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, int ro
     const int c = lane;
     for (int r = wave; r < kCastTile; r += kThreads / 64) {
         const int gr = r0 + r, gc = c0 + c;
-        float v = 0.0f;
-        if (gr < rows && gc < cols) v = g[static_cast<int64_t>(gr) * cols + gc];
-        const double q = static_cast<double>(bf16_to_f32(f32_to_bf16(v))) / d;
+        float v = 0.0f;  // bf16(G) at (gr, gc)
+        if (gr < rows && gc < cols) {
+            if constexpr (BF16IN)
+                v = bf16_to_f32(u16[static_cast<int64_t>(gr) * cols + gc]);
+            else
+                v = bf16_to_f32(f32_to_bf16(g[static_cast<int64_t>(gr) * cols + gc]));
+        }
+        const double q = static_cast<double>(v) / d;
         const bf16_t h = (gr < rows && gc < cols) ? f64_to_bf16(q) : static_cast<bf16_t>(0);
         natm[static_cast<int64_t>(gr) * ld_nat + gc] = h;
         tile[r][c] = h;
@@ -126,8 +190,8 @@ hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, 
     return hipGetLastError();
 }
 
-hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& plan, const double* partials,
-                             float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream) {
+hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
+                             const double* partials, float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream) {
     // G's orientation is X's unless G is tall (then it is X^T's); both are
     // written over their padded extent (padding as zeros)
     const int rows_pad = plan.tall ? plan.np : plan.mp;
@@ -137,9 +201,30 @@ hipError_t launch_scale_cast(const ConstPtrTable& G, int cnt, const Ns5Plan& pla
     const int64_t nat_mat = static_cast<int64_t>(plan.tall ? plan.xt_elems : plan.x_elems);
     const int64_t tr_mat = static_cast<int64_t>(plan.tall ? plan.x_elems : plan.xt_elems);
     const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
-    k_scale_cast<<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
-        G, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb, eps, nat, ld_nat,
-        nat_mat, tr, ld_tr, tr_mat);
+    if (ub)
+        k_scale_cast<true><<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
+            G, ub, ub_mat, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
+            eps, nat, ld_nat, nat_mat, tr, ld_tr, tr_mat);
+    else
+        k_scale_cast<false><<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
+            G, nullptr, 0, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
+            eps, nat, ld_nat, nat_mat, tr, ld_tr, tr_mat);
+    return hipGetLastError();
+}
+
+hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int cnt, int64_t numel, int nb,
+                                float mu, bf16_t* ub, int64_t ub_mat, double* partials, hipStream_t stream) {
+    bool vec = (numel % 4) == 0;
+    for (int i = 0; i < cnt && vec; ++i)
+        vec = ((reinterpret_cast<uintptr_t>(G.p[i]) | reinterpret_cast<uintptr_t>(BUF.p[i])) & 15u) == 0;
+    int64_t chunk = (numel + nb - 1) / nb;
+    if (vec) chunk = (chunk + 3) / 4 * 4;
+    if (vec)
+        k_momentum_norm<true><<<dim3(nb, cnt), kThreads, 0, stream>>>(G, BUF, numel, nb, chunk, mu, ub, ub_mat,
+                                                                       partials);
+    else
+        k_momentum_norm<false><<<dim3(nb, cnt), kThreads, 0, stream>>>(G, BUF, numel, nb, chunk, mu, ub, ub_mat,
+                                                                        partials);
     return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ MAX_GROUP = 128
 
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
-           "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_ns5_batched_timed",
+           "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_momentum_ns5_batched",
+           "muon_ns5_batched_timed",
            "muon_status_string", "muon_last_error")
 
 
@@ -56,9 +57,12 @@ def _load():
     lib.muon_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
                                      ctypes.c_float, vp, sz, vp]
     lib.muon_ns5_batched.restype = ctypes.c_int
-    lib.muon_ns5_batched_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
-                                           ctypes.c_float, vp, sz, vp, ctypes.POINTER(vp), ctypes.c_int,
-                                           ctypes.POINTER(ctypes.c_int)]
+    lib.muon_momentum_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), pi64,
+                                              pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    lib.muon_momentum_ns5_batched.restype = ctypes.c_int
+    lib.muon_ns5_batched_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                           ctypes.c_float, pi64, pi64, i64, ctypes.c_int, ctypes.c_float, vp, sz,
+                                           vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.muon_ns5_batched_timed.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
@@ -195,10 +199,15 @@ def batched_workspace_size(shapes):
     return int(lib.muon_ns5_batched_workspace_size(rows, cols, n))
 
 
-def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None):
+def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None, bufs=None, mu=0.95):
     """NS5 of a list of float32 matrices of any shapes (one device), with one
     launch per product and NS5 step over all matrices that share a tile size.
     Returns the list of outputs (new tensors unless given).
+
+    ``bufs`` (a list of float32 momentum buffers shaped like ``Gs``): run the
+    whole Muon step instead: Gs are gradients, the buffers are updated in
+    place (``buf <- mu*buf + g``) and the outputs are NS5 of
+    ``u = g + mu*buf``, with momentum and the norm fused in one pass.
 
     ``events`` (measurement): a list of ``torch.cuda.Event(enable_timing=True)``
     pairs ``[start0, stop0, start1, stop1, ...]``; the library records them
@@ -227,16 +236,31 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
     g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
     o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
     nbytes = ws.numel() * ws.element_size()
+    b_ptrs = None
+    if bufs is not None:
+        bufs = list(bufs)
+        if len(bufs) != count:
+            raise ValueError("bufs must match Gs in length")
+        for i, (G, b) in enumerate(zip(Gs, bufs)):
+            _require_f32_cuda(b, f"bufs[{i}]")
+            if b.shape != G.shape or b.device != G.device:
+                raise ValueError(f"bufs[{i}] must have the shape and device of Gs[{i}]")
+        b_ptrs = (ctypes.c_void_p * count)(*[b.data_ptr() for b in bufs])
     if events is None:
-        _check(lib.muon_ns5_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps), ws.data_ptr(),
-                                    nbytes, stream))
+        if b_ptrs is None:
+            _check(lib.muon_ns5_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps), ws.data_ptr(),
+                                        nbytes, stream))
+        else:
+            _check(lib.muon_momentum_ns5_batched(g_ptrs, b_ptrs, o_ptrs, rows, cols, count, float(mu), int(steps),
+                                                 float(eps), ws.data_ptr(), nbytes, stream))
     else:
         if len(events) % 2:
             raise ValueError("events must come in (start, stop) pairs")
         ev = (ctypes.c_void_p * max(len(events), 1))(*[e.cuda_event for e in events])
         rec = ctypes.c_int(0)
-        _check(lib.muon_ns5_batched_timed(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps),
-                                          ws.data_ptr(), nbytes, stream, ev, len(events) // 2, ctypes.byref(rec)))
+        _check(lib.muon_ns5_batched_timed(g_ptrs, o_ptrs, b_ptrs, float(mu), rows, cols, count, int(steps),
+                                          float(eps), ws.data_ptr(), nbytes, stream, ev, len(events) // 2,
+                                          ctypes.byref(rec)))
         ns5_batched.last_recorded = rec.value
     return outs
 

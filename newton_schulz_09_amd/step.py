@@ -61,6 +61,14 @@ class MuonStep:
         """Event pairs recorded by the last ``orthogonalise(events=...)``."""
         return muon.ns5_batched.last_recorded
 
+    def fused_step(self, events=None):
+        """The whole step in one call: momentum fused with the first pass of
+        the norm, then NS5; ``us`` is not written (u never exists in
+        float32).  ``events``: see ``muon.ns5_batched``."""
+        muon.ns5_batched(self.grads, self.outs, steps=self.steps, eps=self.eps, workspace=self.workspace,
+                         events=events, bufs=self.bufs, mu=self.mu)
+        return self.outs
+
     def step(self):
         """Enqueue one step on the current stream; results land in ``outs``
         (and the new state in ``bufs``)."""

@@ -137,7 +137,28 @@ def test_batched_validation_errors_before_any_launch(muon):
         == muon.MUON_ERR_UNSUPPORTED
     ev = (ctypes.c_void_p * 1)()
     rec = ctypes.c_int(7)
-    assert lib.muon_ns5_batched_timed(g, o, rows, cols, 2, 5, 1e-7, ws, need, None, None, 1,
+    assert lib.muon_ns5_batched_timed(g, o, None, 0.95, rows, cols, 2, 5, 1e-7, ws, need, None, None, 1,
                                       ctypes.byref(rec)) == muon.MUON_ERR_INVALID_ARG
     assert rec.value == 0
     del fake, ev
+
+
+def test_fused_step_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    b = (ctypes.c_void_p * 2)(0x400000, 0x400100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_ns5_batched_workspace_size(rows, cols, 2)
+    call = lib.muon_momentum_ns5_batched
+    assert call(g, None, o, rows, cols, 2, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    nullb = (ctypes.c_void_p * 2)(0x400000, 0)
+    assert call(g, nullb, o, rows, cols, 2, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"momentum buffer" in lib.muon_last_error()
+    alias = (ctypes.c_void_p * 2)(0x400000, 0x300100)       # out[1] == buf[1]
+    assert call(g, alias, o, rows, cols, 2, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"alias" in lib.muon_last_error()
+    assert call(g, b, o, rows, cols, 2, 0.95, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+    assert call(g, b, o, rows, cols, 0, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG

@@ -223,3 +223,62 @@ def test_batched_zero_steps_and_aliasing(muon):
     muon.ns5_batched(Gs, outs=Gs)            # in place
     for h, g in zip(host, Gs):
         parity.assert_ns5_parity(parity.to_np(g), oracle.ns5(h), "batched in place")
+
+
+
+# ---------------------------------------------------------------- fused Muon step
+
+def test_fused_step_matches_momentum_then_ns5(muon):
+    """muon_momentum_ns5_batched = momentum, then NS5 of u: the new buffers are
+    exact (<= 1 fp32 ulp vs the oracle), the updates meet the parity bar and
+    agree with the unfused path but for rare bf16 ties of the norm."""
+    from newton_schulz_09_amd import step as step_mod
+    shapes = [(64, 128), (128, 64), (65, 130), (130, 65), (3, 5), (300, 768), (768, 300), (1, 7)]
+    rng = np.random.default_rng(21)
+    gs = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    bs = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    fused = step_mod.MuonStep(shapes)
+    plain = step_mod.MuonStep(shapes)
+    for st in (fused, plain):
+        for k in range(len(shapes)):
+            st.grads[k].copy_(torch.from_numpy(gs[k]))
+            st.bufs[k].copy_(torch.from_numpy(bs[k]))
+    for _ in range(2):                      # two steps: the buffer carries over
+        fused.fused_step()
+        plain.step()
+    torch.cuda.synchronize()
+    for k, s in enumerate(shapes):
+        b1, u1 = oracle.momentum_nesterov(gs[k], bs[k], 0.95)
+        b2, u2 = oracle.momentum_nesterov(gs[k], b1, 0.95)
+        assert parity.ulp_diff32(parity.to_np(fused.bufs[k]), b2).max() <= 1
+        assert np.array_equal(parity.to_np(fused.bufs[k]), parity.to_np(plain.bufs[k]))
+        got = parity.to_np(fused.outs[k])
+        parity.assert_ns5_parity(got, oracle.ns5(u2), f"fused {s}")
+        d = parity.bf16_ulp_diff(got, parity.to_np(plain.outs[k]))
+        assert np.mean(d == 0) > 0.99, f"{s}: fused and unfused differ in {np.mean(d != 0):.3%} of entries"
+
+
+def test_fused_step_misaligned_and_ragged(muon):
+    """Buffers that are not 16-byte aligned or not a multiple of 4 long take
+    the scalar path of the fused pass."""
+    rng = np.random.default_rng(5)
+    shapes = [(7, 9), (33, 17)]
+    g_host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    b_host = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    flat_g = torch.zeros(1 + sum(r * c for r, c in shapes), device="cuda")
+    flat_b = torch.zeros_like(flat_g)
+    views_g, views_b, off = [], [], 1       # offset 1 float: 4-byte aligned only
+    for (r, c), gh, bh in zip(shapes, g_host, b_host):
+        vg = flat_g[off:off + r * c].view(r, c)
+        vb = flat_b[off:off + r * c].view(r, c)
+        vg.copy_(torch.from_numpy(gh))
+        vb.copy_(torch.from_numpy(bh))
+        views_g.append(vg)
+        views_b.append(vb)
+        off += r * c
+    outs = muon.ns5_batched(views_g, bufs=views_b, mu=0.9)
+    torch.cuda.synchronize()
+    for k in range(len(shapes)):
+        nb, u = oracle.momentum_nesterov(g_host[k], b_host[k], 0.9)
+        assert parity.ulp_diff32(parity.to_np(views_b[k]), nb).max() <= 1
+        parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(u), f"ragged {shapes[k]}")

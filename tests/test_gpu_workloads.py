@@ -43,6 +43,27 @@ def _run_step(step_mod, items, shapes):
 
 
 @pytest.mark.timeout(900)
+def test_gpt2_124m_fused_step_all_matrices(mods):
+    """GPT-2 124M hidden-matrix set: one fused step (momentum + NS5 in one
+    call, the configuration the benchmark times), every matrix checked."""
+    _, step_mod = mods
+    items = workloads.gpt2_124m()
+    st = step_mod.MuonStep([it[2].shape for it in items])
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    st.fused_step()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for k, (layer, si, G, buf) in enumerate(items):
+        want_b, want_u = oracle.momentum_nesterov(G, buf, 0.95)
+        assert parity.ulp_diff32(parity.to_np(st.bufs[k]), want_b).max() <= 1
+        r = parity.assert_ns5_parity(parity.to_np(st.outs[k]), oracle.ns5(want_u), f"layer {layer} {G.shape}")
+        worst = max(worst, r)
+    print(f"gpt2-124m fused step: worst relative Frobenius error {worst:.3g}", flush=True)
+
+
+@pytest.mark.timeout(900)
 def test_gpt2_124m_step_all_matrices(mods):
     """GPT-2 124M hidden-matrix set: one full step, every matrix checked."""
     _, step_mod = mods
