@@ -110,19 +110,14 @@ bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* p) {
     if (cnt < 1) return false;
     p->cnt = static_cast<int>(cnt);
     p->ldx = p->np + ld_skew();
-    p->ldxt = p->mp + ld_skew();
     p->lda = p->mp + ld_skew();
     p->x_elems = static_cast<size_t>(p->mp) * p->ldx;
-    p->xt_elems = static_cast<size_t>(p->np) * p->ldxt;
     p->a_elems = static_cast<size_t>(p->mp) * p->lda;
     size_t off = 0;
     const size_t xb = align256(cnt * p->x_elems * sizeof(bf16_t));
-    const size_t xtb = align256(cnt * p->xt_elems * sizeof(bf16_t));
     const size_t ab = align256(cnt * p->a_elems * sizeof(bf16_t));
     p->off_x[0] = off; off += xb;
     p->off_x[1] = off; off += xb;
-    p->off_xt[0] = off; off += xtb;
-    p->off_xt[1] = off; off += xtb;
     p->off_a = off; off += ab;
     p->off_b = off; off += ab;
     p->off_part = off; off += align256(cnt * p->nb * sizeof(double));
@@ -226,7 +221,7 @@ int check_workspace(void* ws, size_t ws_bytes, size_t need) {
 
 // Workspace pointers of one chunk.
 struct ChunkBufs {
-    bf16_t *X[2], *XT[2], *A, *B;
+    bf16_t *X[2], *A, *B;
     double* part;
 };
 
@@ -236,8 +231,6 @@ ChunkBufs bufs_of(char* ws, const Chunk& c) {
     ChunkBufs r;
     r.X[0] = reinterpret_cast<bf16_t*>(b + p.off_x[0]);
     r.X[1] = reinterpret_cast<bf16_t*>(b + p.off_x[1]);
-    r.XT[0] = reinterpret_cast<bf16_t*>(b + p.off_xt[0]);
-    r.XT[1] = reinterpret_cast<bf16_t*>(b + p.off_xt[1]);
     r.A = reinterpret_cast<bf16_t*>(b + p.off_a);
     r.B = reinterpret_cast<bf16_t*>(b + p.off_b);
     r.part = reinterpret_cast<double*>(b + p.off_part);
@@ -281,14 +274,12 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 e = launch_sumsq(gt, pl.cnt, pl.rows * pl.cols, pl.nb, b.part, stream);
                 if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
             }
-            bf16_t* nat = pl.tall ? b.XT[0] : b.X[0];
-            bf16_t* tr = pl.tall ? b.X[0] : b.XT[0];
-            e = launch_scale_cast(gt, ub, ub_mat, pl.cnt, pl, b.part, eps, nat, tr, stream);
+            e = launch_scale_cast(gt, ub, ub_mat, pl.cnt, pl, b.part, eps, b.X[0], stream);
             if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
             if (steps == 0) {
                 PtrTable ot{};
                 for (int i = 0; i < pl.cnt; ++i) ot.p[i] = c.out[i];
-                e = launch_copy_out(pl, pl.cnt, nat, ot, stream);
+                e = launch_copy_out(pl, pl.cnt, b.X[0], ot, stream);
                 if (e != hipSuccess) return hip_fail(e, "copy-out launch");
             }
         }
@@ -321,7 +312,7 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 ChunkBufs b = bufs_of(ws, c);
                 const int T = pl.tile;
                 const int tiles_m = pl.mp / T;
-                const int64_t xe = static_cast<int64_t>(pl.x_elems), xte = static_cast<int64_t>(pl.xt_elems);
+                const int64_t xe = static_cast<int64_t>(pl.x_elems);
                 const int64_t ae = static_cast<int64_t>(pl.a_elems);
                 // A = X X^T
                 GemmArgs& g1 = syrk.seg[ci];
@@ -348,15 +339,14 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g3.first_block = nb_bx;
                 g3.out_base = out_base[ci];
                 g3.P = b.B; g3.p_mat = ae; g3.ldp = pl.lda;
-                g3.Q = b.XT[cur]; g3.q_mat = xte; g3.ldq = pl.ldxt;
+                g3.Q = b.X[cur]; g3.q_mat = xe; g3.ldq = pl.ldx;  // NN: X read as is
                 g3.kpad = static_cast<int>(round_up(pl.m, 64));
                 const int btm = pl.mp / bx_tile, btn = pl.np / bx_tile;
                 g3.tiles = btm; g3.tiles_n = btn; g3.tiles_per_mat = btm * btn;
                 g3.band = band_rows(btm);
-                g3.E = b.XT[cur]; g3.e_mat = xte; g3.lde = pl.ldxt;
+                g3.E = b.X[cur]; g3.e_mat = xe; g3.lde = pl.ldx;
                 g3.alpha = MUON_NS5_A; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
-                g3.CT = b.XT[nxt]; g3.ct_mat = xte; g3.ldct = pl.ldxt;
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
             }

@@ -5,12 +5,15 @@
 //     B = b A + c A A        (A is symmetric, so A A = A A^T; upper tiles,
 //                             mirrored; the b A + c (.) update is fused)
 //     X' = a X + B X         (full tile grid; a X + (.) fused; X' is stored
-//                             in both orientations for the next step, or as
-//                             float32 in G's orientation after the last step)
+//                             row-major for the next step, or as float32 in
+//                             G's orientation after the last step)
 //
-// All three are "NT" products  C[i][j] = sum_k P[i][k] Q[j][k]  with both
-// operands contiguous along k, which is the operand layout of the CDNA
-// matrix cores.
+// The symmetric two are "NT" products  C[i][j] = sum_k P[i][k] Q[j][k]  with
+// both operands contiguous along k, the operand layout of the CDNA matrix
+// cores.  a X + B X is "NN": its second operand X is row-major (contiguous
+// along n, not k); its tiles are stored row-major in LDS and the MFMA
+// fragments are formed with gfx950's transposing LDS reads
+// (ds_read_b64_tr_b16), so X is never stored transposed.
 //
 // Engine (gfx950): 256 threads = 4 wavefronts of 64 lanes in a 2x2
 // arrangement, each wave owning a (BM/2)x(BN/2) sub-tile built from 32x32
@@ -70,6 +73,40 @@ __device__ __forceinline__ int swz(int r) {
     else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// Slot permutation of row r of a row-major K x N tile (CPRQ chunks per row)
+// read with transposing reads: the 8 rows one read touches (two runs of 4,
+// 8 apart) get distinct offsets.
+template <int CPRQ>
+__device__ __forceinline__ int swq(int r) {
+    return ((((r & 3) << 1) | ((r >> 3) & 1)) * (CPRQ / 8)) & (CPRQ - 1);
+}
+
+
+// ds_read_b64_tr_b16: in every group of 16 lanes, lane r supplies the LDS
+// address of 4 consecutive 16-bit values (row r of a 16 x 4 block R); lane i
+// receives R[4e + i/4][i%4] for e = 0..3.  With lane r pointing at
+// (k + r/4, c + 4 (r%4)) of a row-major tile, lane i receives the four values
+// (k .. k+3, c + i): four consecutive K of one column.
+//
+// Issued as inline asm: the compiler's wait insertion cannot tell that these
+// reads do not overlap the global->LDS loads in flight and would otherwise
+// wait for all of them first.  The asm is invisible to that pass, so every
+// consumer waits explicitly (lgkm_wait_tie) before using the result.
+__device__ __forceinline__ u32x2 lds_read_tr4(const bf16_t* p) {
+    const uint32_t a = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)(p)));
+    uint64_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Wait for this wave's LDS reads, with `x` passing through the wait so that
+// no use of it can be scheduled before it.
+template <typename T>
+__device__ __forceinline__ void lgkm_wait_tie(T& x) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x));
+}
+
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and its LDS operations are done, then barrier.  Written as one
 // asm statement with a memory clobber so the compiler keeps LDS accesses on
@@ -87,13 +124,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
     constexpr int WTM = BM / 2, WTN = BN / 2;  // wave sub-tile
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row
+    // a X + B X reads its second operand, X, in its own row-major layout ("NN"):
+    // the Q tile is BK rows of K by BN columns, and the MFMA fragments (8
+    // consecutive K of one column per lane) come from transposing LDS reads
+    constexpr bool NN = (KIND == GEMM_BX || KIND == GEMM_BX_FINAL);
+    constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row (NT tiles)
     constexpr int RPI = 64 / CPR;          // rows filled by one wave-wide 1 KB load
+    constexpr int CPRQ = NN ? BN / 8 : CPR;  // the same for the Q tile
+    constexpr int RPIQ = 64 / CPRQ;
     constexpr int IP = BM / RPI / 4;       // loads per wave per stage, P operand
-    constexpr int IQ = BN / RPI / 4;       // and Q operand
+    constexpr int IQ = NN ? BK / RPIQ / 4 : BN / RPI / 4;  // and Q operand
     constexpr int NLOAD = IP + IQ;
     constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
-    static_assert(IP >= 1 && IQ >= 1, "tile too small for the loader");
+    static_assert(IP >= 1 && IQ >= 1 && RPIQ >= 1, "tile shape not supported by the loader");
     static_assert(BM * BN <= STAGES * STAGE, "the epilogue reuses the stages as four wave sub-tiles");
 
     __shared__ __attribute__((aligned(1024))) bf16_t lds[STAGES * STAGE];
@@ -140,17 +183,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     const bf16_t* gq[IQ];
     {
         const bf16_t* P = args.P + mat * args.p_mat + static_cast<int64_t>(i0) * args.ldp;
-        const bf16_t* Q = args.Q + mat * args.q_mat + static_cast<int64_t>(j0) * args.ldq;
         const int lr = lane / CPR, ls = lane % CPR;
 #pragma unroll
         for (int i = 0; i < IP; ++i) {
             const int row = (wave * IP + i) * RPI + lr;
             gp[i] = P + static_cast<int64_t>(row) * args.ldp + ((ls ^ swz<CPR>(row)) << 3);
         }
+        if constexpr (NN) {
+            // Q rows are K rows of X; the tile's columns start at j0
+            const bf16_t* Q = args.Q + mat * args.q_mat + j0;
+            const int lrq = lane / CPRQ, lsq = lane % CPRQ;
 #pragma unroll
-        for (int i = 0; i < IQ; ++i) {
-            const int row = (wave * IQ + i) * RPI + lr;
-            gq[i] = Q + static_cast<int64_t>(row) * args.ldq + ((ls ^ swz<CPR>(row)) << 3);
+            for (int i = 0; i < IQ; ++i) {
+                const int row = (wave * IQ + i) * RPIQ + lrq;
+                gq[i] = Q + static_cast<int64_t>(row) * args.ldq + ((lsq ^ swq<CPRQ>(row)) << 3);
+            }
+        } else {
+            const bf16_t* Q = args.Q + mat * args.q_mat + static_cast<int64_t>(j0) * args.ldq;
+#pragma unroll
+            for (int i = 0; i < IQ; ++i) {
+                const int row = (wave * IQ + i) * RPI + lr;
+                gq[i] = Q + static_cast<int64_t>(row) * args.ldq + ((ls ^ swz<CPR>(row)) << 3);
+            }
         }
     }
     // load L (< IP: P rows, else Q rows) of K step kt into LDS stage `stage`
@@ -160,10 +214,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
         if (L < IP)
             __builtin_amdgcn_global_load_lds((global_cptr)(gp[L] + k0),
                                              (lds_ptr)(sP + (wave * IP + L) * RPI * BK), 16, 0, 0);
+        else if constexpr (NN)
+            __builtin_amdgcn_global_load_lds((global_cptr)(gq[L - IP] + static_cast<int64_t>(k0) * args.ldq),
+                                             (lds_ptr)(sP + BM * BK + (wave * IQ + L - IP) * RPIQ * BN), 16, 0,
+                                             0);
         else
             __builtin_amdgcn_global_load_lds((global_cptr)(gq[L - IP] + k0),
                                              (lds_ptr)(sP + BM * BK + (wave * IQ + L - IP) * RPI * BK), 16, 0,
                                              0);
+    };
+
+    // NN Q fragments: lane l (group g = l/16, r = l%16) points at K row
+    // 16 kk + 8 (g/2) + r/4 (+4 for the second half) and column
+    // 16 (g%2) + 4 (r%4) of the 32-column fragment; the row's slot
+    // permutation is the same for every kk and both halves.
+    const int tq_g = lane >> 4, tq_r = lane & 15;
+    const int tq_row = 8 * (tq_g >> 1) + (tq_r >> 2);                // + 16 kk (+ 4)
+    const int tq_col = 16 * (tq_g & 1) + 4 * (tq_r & 3);             // + column of the fragment
+    const int tq_sw = swq<CPRQ>(tq_row);
+    auto q_frag_nn = [&](const bf16_t* sQs, int kk, int col0) -> bf16x8 {
+        const int col = col0 + tq_col;
+        const bf16_t* p0 = sQs + (16 * kk + tq_row) * BN + ((((col >> 3) ^ tq_sw)) << 3) + (col & 7);
+        const u32x2 lo = lds_read_tr4(p0);
+        const u32x2 hi = lds_read_tr4(p0 + 4 * BN);
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
     };
 
     // ---- fragment reads: lane l reads row (l % 32) of a 32-row fragment,
@@ -185,13 +259,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-    // The epilogue's second operand (AAB: A[j][i]; BX: old X[i][j] = X^T[j][i])
+    // The epilogue's second operand (AAB: A[j][i] = A[i][j]; BX: old X[i][j])
     // is the K slice [i0, i0 + BM) of the Q operand, which passes through LDS
     // during the K loop: for tiles up to 128 each wave copies its values out of
     // the stage of the matching K step, so they are never read from memory
-    // again.  K steps past kpad hold only padding, whose values are zero.
-    constexpr bool CAPTURE_E =
-        (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) && BM <= 128;
+    // again (for 256 tiles the copies would not fit in registers).  K steps
+    // past kpad hold only padding, whose values are zero.
+    constexpr bool CAPTURE_E = (NN || KIND == GEMM_AAB) && BM <= 128;
     u32x2 ev[CAPTURE_E ? FM : 1][CAPTURE_E ? FN : 1][4];
     if constexpr (CAPTURE_E) {
 #pragma unroll
@@ -234,16 +308,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
 
         const bf16_t* sP = lds + (kt % STAGES) * STAGE + wm * WTM * BK;
         const bf16_t* sQ = lds + (kt % STAGES) * STAGE + BM * BK + wn * WTN * BK;
+        const bf16_t* sQs_nn = lds + (kt % STAGES) * STAGE + BM * BK;  // NN: the whole Q tile
         bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             a[0][fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(sP + fm * 32 * BK + soff[0]));
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            b[0][fn] = as_bf16x8(*reinterpret_cast<const u32x4*>(sQ + fn * 32 * BK + soff[0]));
+        for (int fn = 0; fn < FN; ++fn) {
+            if constexpr (NN)
+                b[0][fn] = q_frag_nn(sQs_nn, 0, wn * WTN + fn * 32);
+            else
+                b[0][fn] = as_bf16x8(*reinterpret_cast<const u32x4*>(sQ + fn * 32 * BK + soff[0]));
+        }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int c = kk & 1, n = c ^ 1;
+            if constexpr (NN) {
+                // the transposing reads of this slice's Q fragments are asm
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) lgkm_wait_tie(b[c][fn]);
+            }
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -257,6 +342,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                             if (r < FM)
                                 a[n][r] = as_bf16x8(
                                     *reinterpret_cast<const u32x4*>(sP + r * 32 * BK + soff[kk + 1]));
+                            else if constexpr (NN)
+                                b[n][r - FM] = q_frag_nn(sQs_nn, kk + 1, wn * WTN + (r - FM) * 32);
                             else
                                 b[n][r - FM] = as_bf16x8(
                                     *reinterpret_cast<const u32x4*>(sQ + (r - FM) * 32 * BK + soff[kk + 1]));
@@ -279,12 +366,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                     const int kin = ik - kt * BK;
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn) {
-                        const int jrow = wn * WTN + fn * 32 + (lane & 31);
+                        if constexpr (NN) {
+                            // X rows kin + 8 g4 + 4 (l/32) .. +3 at column (l % 32) of
+                            // this fragment: one transposing read per g4
+                            const int col = wn * WTN + fn * 32 + tq_col;
 #pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const int kk = kin + 8 * g4 + 4 * (lane >> 5);
-                            ev[fm][fn][g4] = *reinterpret_cast<const u32x2*>(
-                                sQs + jrow * BK + (((kk >> 3) ^ swz<CPR>(jrow)) << 3) + (kk & 7));
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                const int krow = kin + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
+                                ev[fm][fn][g4] = lds_read_tr4(
+                                    sQs + krow * BN + (((col >> 3) ^ swq<CPRQ>(krow)) << 3) + (col & 7));
+                            }
+                        } else {
+                            const int jrow = wn * WTN + fn * 32 + (lane & 31);
+#pragma unroll
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                const int kk = kin + 8 * g4 + 4 * (lane >> 5);
+                                ev[fm][fn][g4] = *reinterpret_cast<const u32x2*>(
+                                    sQs + jrow * BK + (((kk >> 3) ^ swz<CPR>(jrow)) << 3) + (kk & 7));
+                            }
                         }
                     }
                 }
@@ -299,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     // runs of 4 consecutive rows in one column.  The fused update is applied
     // in registers and rounded once to bf16; then every wave passes its
     // (WTM x WTN) sub-tile through its own LDS region to store whole rows with
-    // 16-byte stores: once transposed (X^T for the a X + B X product, the
-    // mirror block for the symmetric ones) and once as is.
+    // 16-byte stores: as is, and for the symmetric products also transposed
+    // into the mirror block.
     const int64_t cm = static_cast<int64_t>(mat);
     const int i0w = i0 + wm * WTM, j0w = j0 + wn * WTN;  // this wave's sub-tile origin
     u32x2 hv[FM][FN][4];                                  // 4 bf16 (rows ib..ib+3, column j)
@@ -318,11 +417,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                     // AAB: A[i][j] = A[j][i] (symmetric); BX: old X[i][j] =
                     // X^T[j][i].  Either way a contiguous run of 4 along i.
                     u32x2 e4;
-                    if constexpr (CAPTURE_E)
+                    if constexpr (CAPTURE_E) {
+                        if constexpr (NN) lgkm_wait_tie(ev[fm][fn][g4]);  // captured by asm reads
                         e4 = ev[fm][fn][g4];
-                    else
+                    } else if constexpr (NN) {
+                        // old X[ib..ib+3][j], row-major: 2-byte loads (the 32 lanes
+                        // of a half-wave read 64 contiguous bytes of one row)
+                        const bf16_t* e = args.E + cm * args.e_mat + static_cast<int64_t>(ib) * args.lde + j;
+                        e4.x = static_cast<uint32_t>(e[0]) | (static_cast<uint32_t>(e[args.lde]) << 16);
+                        e4.y = static_cast<uint32_t>(e[2 * args.lde]) | (static_cast<uint32_t>(e[3 * args.lde]) << 16);
+                    } else {
                         e4 = *reinterpret_cast<const u32x2*>(args.E + cm * args.e_mat +
                                                              static_cast<int64_t>(j) * args.lde + ib);
+                    }
                     const float e0 = bf16_to_f32(static_cast<bf16_t>(e4.x & 0xffffu));
                     const float e1 = bf16_to_f32(static_cast<bf16_t>(e4.x >> 16));
                     const float e2 = bf16_to_f32(static_cast<bf16_t>(e4.y & 0xffffu));
@@ -427,10 +534,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
         }
         // (wm > wn on a diagonal tile: the mirror of the wm < wn block)
     } else if constexpr (KIND == GEMM_BX) {
-        put_t();
-        lds_fence();
-        store_bf16(WTN, CT_, 0, args.CT + cm * args.ct_mat + static_cast<int64_t>(j0w) * args.ldct + i0w, args.ldct);
-        lds_fence();
         put_n(false);
         lds_fence();
         store_bf16(WTM, CN_, 2, args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);

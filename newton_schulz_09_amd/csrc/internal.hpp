@@ -16,15 +16,14 @@ namespace muon {
 // (zero rows/columns of X give zero rows/columns of A, B and the next X), so
 // the GEMMs run on whole tiles with no edge predication.
 //
-// Per matrix the workspace holds, all bf16:
-//   X[2]  (mp x np, row-major)  and  XT[2] (np x mp): the iterate in both
-//         orientations, ping-ponged between steps, so that every product is
-//         a "both operands contiguous along K" (NT) product:
-//             A  = X  . X^T   -> NT(X,  X)     K = n
-//             AA = A  . A^T   -> NT(A,  A)     K = m   (A is symmetric)
-//             BX = B  . X     -> NT(B,  XT)    K = m
-//   A, B  (mp x mp)
-// plus float64 partial sums of squares for the Frobenius norm.
+// Per matrix the workspace holds:
+//   X[2]  (mp x ldx, bf16, row-major): the iterate, ping-ponged between
+//         steps.  A = X X^T is an NT product (both operands contiguous along
+//         n); B X reads X as is (NN, through transposing LDS reads), so X is
+//         never stored transposed.  X[1] also stages bf16(u) in the fused
+//         Muon step until step 1 overwrites it.
+//   A, B  (mp x lda, bf16)
+//   float64 partial sums of squares for the Frobenius norm.
 struct Ns5Plan {
     int64_t rows, cols;
     int m, n;
@@ -33,12 +32,12 @@ struct Ns5Plan {
     int mp, np;
     int nb;    // norm partials per matrix
     int cnt;   // matrices per pass
-    // row strides (elements) of X (mp rows), X^T (np rows) and A, B (mp rows):
-    // the padded widths plus a skew that keeps rows of power-of-two widths
-    // from all starting on the same memory channel
-    int ldx, ldxt, lda;
-    size_t x_elems, xt_elems, a_elems;  // per-matrix element counts
-    size_t off_x[2], off_xt[2], off_a, off_b, off_part;  // byte offsets
+    // row strides (elements) of X (mp rows) and A, B (mp rows): the padded
+    // widths plus a skew that keeps rows of power-of-two widths from all
+    // starting on the same memory channel
+    int ldx, lda;
+    size_t x_elems, a_elems;  // per-matrix element counts
+    size_t off_x[2], off_a, off_b, off_part;  // byte offsets
     size_t bytes;
 };
 
@@ -69,9 +68,6 @@ struct GemmArgs {
     bf16_t* C;
     int64_t c_mat;
     int ldc;
-    bf16_t* CT;
-    int64_t ct_mat;
-    int ldct;
     const bf16_t* E;
     int64_t e_mat;
     int lde;
@@ -90,16 +86,17 @@ hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, 
 hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, double* partials,
                         hipStream_t stream);
 
-// ub (if non-null): dense bf16 copies of the inputs (stride ub_mat per
-// matrix) to cast from instead of the float32 G.
+// Writes X0 into X (the transpose of G when G is tall).  ub (if non-null):
+// dense bf16 copies of the inputs (stride ub_mat per matrix) to cast from
+// instead of the float32 G.
 hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
-                             const double* partials, float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream);
+                             const double* partials, float eps, bf16_t* X, hipStream_t stream);
 
 hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int cnt, int64_t numel, int nb,
                                 float mu, bf16_t* ub, int64_t ub_mat, double* partials, hipStream_t stream);
 
-hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
-                           hipStream_t stream);
+// out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
+hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream);
 
 hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
                        hipStream_t stream);

@@ -11,10 +11,11 @@
 //                The split of G into workgroups is fixed, so the result is
 //                deterministic (no atomics).
 //   k_scale_cast reduces a matrix's partials in a fixed order (every
-//                workgroup gets the same float64 norm), then reads G again and
-//                writes X0 = bf16( bf16(G) / (||G|| + eps) ) twice: in G's own
-//                orientation and transposed through an LDS tile (6 B/elem
-//                with 4 B read).  The quotient is formed in float64 and
+//                workgroup gets the same float64 norm), then reads G again
+//                (or its bf16 staging copy) and writes
+//                X0 = bf16( bf16(G) / (||G|| + eps) ) in the iteration's
+//                orientation: directly, or transposed through an LDS tile
+//                when G is tall.  The quotient is formed in float64 and
 //                rounded once to bf16.  Padding to the GEMM tile is written
 //                as zeros.
 #include "internal.hpp"
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const 
     __syncthreads();
     const double d = s_norm;
 
-    bf16_t* natm = nat + static_cast<int64_t>(mat) * nat_mat;
-    bf16_t* trm = tr + static_cast<int64_t>(mat) * tr_mat;
+    bf16_t* natm = nat ? nat + static_cast<int64_t>(mat) * nat_mat : nullptr;
+    bf16_t* trm = tr ? tr + static_cast<int64_t>(mat) * tr_mat : nullptr;
 
     // G's orientation: lanes run along the columns (coalesced reads/writes)
     const int c = lane;
@@ -157,9 +158,10 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const 
         }
         const double q = static_cast<double>(v) / d;
         const bf16_t h = (gr < rows && gc < cols) ? f64_to_bf16(q) : static_cast<bf16_t>(0);
-        natm[static_cast<int64_t>(gr) * ld_nat + gc] = h;
+        if (natm) natm[static_cast<int64_t>(gr) * ld_nat + gc] = h;
         tile[r][c] = h;
     }
+    if (!trm) return;  // uniform across the workgroup
     __syncthreads();
     // transposed: lanes run along G's rows, which are the columns of tr
     const int r = lane;
@@ -168,16 +170,16 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const 
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int ld_nat,
-                                                       const bf16_t* nat, int64_t nat_mat) {
+__global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int tall, int ldx,
+                                                       const bf16_t* X, int64_t x_mat) {
     const int mat = blockIdx.y;
     const int64_t total = static_cast<int64_t>(rows) * cols;
-    const bf16_t* src = nat + static_cast<int64_t>(mat) * nat_mat;
+    const bf16_t* src = X + static_cast<int64_t>(mat) * x_mat;
     float* dst = out.p[mat];
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const int64_t r = i / cols, c = i - r * cols;
-        dst[i] = bf16_to_f32(src[r * ld_nat + c]);
+        const int64_t r = i / cols, c = i - r * cols;  // position in G's orientation
+        dst[i] = bf16_to_f32(tall ? src[c * ldx + r] : src[r * ldx + c]);
     }
 }
 
@@ -191,15 +193,16 @@ hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, 
 }
 
 hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
-                             const double* partials, float eps, bf16_t* nat, bf16_t* tr, hipStream_t stream) {
-    // G's orientation is X's unless G is tall (then it is X^T's); both are
-    // written over their padded extent (padding as zeros)
+                             const double* partials, float eps, bf16_t* X, hipStream_t stream) {
+    // X is G's orientation unless G is tall (then it is G^T): written over its
+    // padded extent (padding as zeros), directly or through the transposing
+    // LDS tile
     const int rows_pad = plan.tall ? plan.np : plan.mp;
     const int cols_pad = plan.tall ? plan.mp : plan.np;
-    const int ld_nat = plan.tall ? plan.ldxt : plan.ldx;
-    const int ld_tr = plan.tall ? plan.ldx : plan.ldxt;
-    const int64_t nat_mat = static_cast<int64_t>(plan.tall ? plan.xt_elems : plan.x_elems);
-    const int64_t tr_mat = static_cast<int64_t>(plan.tall ? plan.x_elems : plan.xt_elems);
+    bf16_t* nat = plan.tall ? nullptr : X;
+    bf16_t* tr = plan.tall ? X : nullptr;
+    const int ld_nat = plan.ldx, ld_tr = plan.ldx;
+    const int64_t nat_mat = static_cast<int64_t>(plan.x_elems), tr_mat = static_cast<int64_t>(plan.x_elems);
     const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
     if (ub)
         k_scale_cast<true><<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
@@ -228,15 +231,13 @@ hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int
     return hipGetLastError();
 }
 
-hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* nat, const PtrTable& out,
-                           hipStream_t stream) {
-    const int ld_nat = plan.tall ? plan.ldxt : plan.ldx;
-    const int64_t nat_mat = static_cast<int64_t>(plan.tall ? plan.xt_elems : plan.x_elems);
+hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream) {
     const int64_t total = plan.rows * plan.cols;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 2048) blocks = 2048;
     k_copy_out<<<dim3(static_cast<unsigned>(blocks), cnt), kThreads, 0, stream>>>(
-        out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), ld_nat, nat, nat_mat);
+        out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), plan.tall ? 1 : 0, plan.ldx, X,
+        static_cast<int64_t>(plan.x_elems));
     return hipGetLastError();
 }
 
