@@ -117,11 +117,15 @@ constexpr int kCastTile = 64;
 
 // BF16IN: the input is the dense bf16 staging copy written by
 // k_momentum_norm (already bf16(G)); otherwise the float32 G of the table.
+// One workgroup per 64x64 tile of G: each thread handles runs of 8
+// consecutive columns (16-byte accesses where the shape allows), and a tall
+// G's tile is transposed through LDS so that X rows are also written 16
+// bytes at a time.
 template <bool BF16IN>
 __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const bf16_t* ub, int64_t ub_mat, int rows,
                                                          int cols, int tiles_c, const double* partials, int nb,
-                                                         float eps, bf16_t* nat, int ld_nat, int64_t nat_mat,
-                                                         bf16_t* tr, int ld_tr, int64_t tr_mat) {
+                                                         float eps, bf16_t* X, int ldx, int64_t x_mat, int tall) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
     const int mat = blockIdx.y;
     const int tr_i = blockIdx.x / tiles_c, tc_i = blockIdx.x % tiles_c;
     const int r0 = tr_i * kCastTile, c0 = tc_i * kCastTile;
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     __shared__ double s_norm;
-    __shared__ bf16_t tile[kCastTile][kCastTile + 2];
+    __shared__ __attribute__((aligned(16))) bf16_t tile_t[kCastTile][kCastTile + 8];  // [col][row]
 
     if (wave == 0) {
         const double* part = partials + static_cast<int64_t>(mat) * nb;
@@ -141,32 +145,72 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const 
     }
     __syncthreads();
     const double d = s_norm;
+    bf16_t* Xm = X + static_cast<int64_t>(mat) * x_mat;
+    // 16-byte loads need every row start aligned: cols a multiple of 8 (bf16)
+    // or 4 (float32), and the base aligned
+    const bool vec = BF16IN ? ((cols & 7) == 0 && (reinterpret_cast<uintptr_t>(u16) & 15u) == 0)
+                            : ((cols & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15u) == 0);
 
-    bf16_t* natm = nat ? nat + static_cast<int64_t>(mat) * nat_mat : nullptr;
-    bf16_t* trm = tr ? tr + static_cast<int64_t>(mat) * tr_mat : nullptr;
-
-    // G's orientation: lanes run along the columns (coalesced reads/writes)
-    const int c = lane;
-    for (int r = wave; r < kCastTile; r += kThreads / 64) {
-        const int gr = r0 + r, gc = c0 + c;
-        float v = 0.0f;  // bf16(G) at (gr, gc)
-        if (gr < rows && gc < cols) {
-            if constexpr (BF16IN)
-                v = bf16_to_f32(u16[static_cast<int64_t>(gr) * cols + gc]);
-            else
-                v = bf16_to_f32(f32_to_bf16(g[static_cast<int64_t>(gr) * cols + gc]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = threadIdx.x + h * kThreads;  // 0 .. 511
+        const int r = idx >> 3, cg = (idx & 7) * 8;  // tile row, first of 8 columns
+        const int gr = r0 + r, gc = c0 + cg;
+        float v[8];
+        if (gr < rows && vec && gc + 8 <= cols) {
+            if constexpr (BF16IN) {
+                const u32x4v w = *reinterpret_cast<const u32x4v*>(u16 + static_cast<int64_t>(gr) * cols + gc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = bf16_to_f32(static_cast<bf16_t>(w[e] & 0xffffu));
+                    v[2 * e + 1] = bf16_to_f32(static_cast<bf16_t>(w[e] >> 16));
+                }
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(g + static_cast<int64_t>(gr) * cols + gc);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(g + static_cast<int64_t>(gr) * cols + gc + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = bf16_to_f32(f32_to_bf16(lo[e]));
+                    v[4 + e] = bf16_to_f32(f32_to_bf16(hi[e]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[e] = 0.0f;
+                if (gr < rows && gc + e < cols) {
+                    if constexpr (BF16IN)
+                        v[e] = bf16_to_f32(u16[static_cast<int64_t>(gr) * cols + gc + e]);
+                    else
+                        v[e] = bf16_to_f32(f32_to_bf16(g[static_cast<int64_t>(gr) * cols + gc + e]));
+                }
+            }
         }
-        const double q = static_cast<double>(v) / d;
-        const bf16_t h = (gr < rows && gc < cols) ? f64_to_bf16(q) : static_cast<bf16_t>(0);
-        if (natm) natm[static_cast<int64_t>(gr) * ld_nat + gc] = h;
-        tile[r][c] = h;
+        // X0 = bf16(bf16(G) / d): the quotient in float64, one rounding;
+        // padding stays zero (0 / d = 0)
+        bf16_t hx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hx[e] = f64_to_bf16(static_cast<double>(v[e]) / d);
+        if (!tall) {
+            u32x4v w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = static_cast<uint32_t>(hx[2 * e]) | (static_cast<uint32_t>(hx[2 * e + 1]) << 16);
+            *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(gr) * ldx + gc) = w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tile_t[cg + e][r] = hx[e];
+        }
     }
-    if (!trm) return;  // uniform across the workgroup
+    if (!tall) return;  // uniform across the workgroup
     __syncthreads();
-    // transposed: lanes run along G's rows, which are the columns of tr
-    const int r = lane;
-    for (int cc = wave; cc < kCastTile; cc += kThreads / 64) {
-        trm[static_cast<int64_t>(c0 + cc) * ld_tr + r0 + r] = tile[r][cc];
+    // X = G^T: X row c0 + c holds G column c0 + c; 8 consecutive G rows per thread
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = threadIdx.x + h * kThreads;
+        const int c = idx >> 3, rg = (idx & 7) * 8;
+        const u32x4v w = *reinterpret_cast<const u32x4v*>(&tile_t[c][rg]);
+        *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(c0 + c) * ldx + r0 + rg) = w;
     }
 }
 
@@ -194,24 +238,22 @@ hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, 
 
 hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
                              const double* partials, float eps, bf16_t* X, hipStream_t stream) {
-    // X is G's orientation unless G is tall (then it is G^T): written over its
-    // padded extent (padding as zeros), directly or through the transposing
-    // LDS tile
+    // X is G's orientation unless G is tall (then it is G^T), written over its
+    // padded extent (padding as zeros)
     const int rows_pad = plan.tall ? plan.np : plan.mp;
     const int cols_pad = plan.tall ? plan.mp : plan.np;
-    bf16_t* nat = plan.tall ? nullptr : X;
-    bf16_t* tr = plan.tall ? X : nullptr;
-    const int ld_nat = plan.ldx, ld_tr = plan.ldx;
-    const int64_t nat_mat = static_cast<int64_t>(plan.x_elems), tr_mat = static_cast<int64_t>(plan.x_elems);
     const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
+    const dim3 grid(tiles_r * tiles_c, cnt);
     if (ub)
-        k_scale_cast<true><<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
-            G, ub, ub_mat, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
-            eps, nat, ld_nat, nat_mat, tr, ld_tr, tr_mat);
+        k_scale_cast<true><<<grid, kThreads, 0, stream>>>(G, ub, ub_mat, static_cast<int>(plan.rows),
+                                                          static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
+                                                          eps, X, plan.ldx, static_cast<int64_t>(plan.x_elems),
+                                                          plan.tall ? 1 : 0);
     else
-        k_scale_cast<false><<<dim3(tiles_r * tiles_c, cnt), kThreads, 0, stream>>>(
-            G, nullptr, 0, static_cast<int>(plan.rows), static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
-            eps, nat, ld_nat, nat_mat, tr, ld_tr, tr_mat);
+        k_scale_cast<false><<<grid, kThreads, 0, stream>>>(G, nullptr, 0, static_cast<int>(plan.rows),
+                                                           static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
+                                                           eps, X, plan.ldx, static_cast<int64_t>(plan.x_elems),
+                                                           plan.tall ? 1 : 0);
     return hipGetLastError();
 }
 
