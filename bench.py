@@ -65,9 +65,9 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": None,
-    "fetch_bytes": None,
-    "write_bytes": None,
+    "sources_sha256": "08400c7cb5a6688284c58cbc4ba7405d8944242765675ea1807cf3766763369a",
+    "fetch_bytes": 292389900,
+    "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
                    "newton_schulz_09_amd/csrc/internal.hpp", "newton_schulz_09_amd/csrc/common.hpp")
