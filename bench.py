@@ -143,7 +143,7 @@ def time_dominant_kernel(st, steps, torch):
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     return {
         "bound": "mfma",
-        "kernel": "k_gemm_nt<128, 128, 64, 2, GEMM_BX>: X' = a X + B X of NS5 steps 1-4, one launch over all "
+        "kernel": "k_gemm_nt<256, 256, 64, 2, 2, 4, GEMM_BX> (256x256 tiles, 8 waves): X' = a X + B X of NS5 steps 1-4, one launch over all "
                   "48 matrices",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,

@@ -285,18 +285,28 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
         }
         if (steps == 0) continue;
 
-        // tile of the a X + B X product: the group's, or 256 when every chunk's
-        // padded sizes allow it (MUON_BX_TILE=256, for tuning)
-        int bx_tile = grp.tile;
-        {
+        // tile of the a X + B X product (rows x columns of the output).  With
+        // 128-tiled groups a larger tile wherever every chunk's padded sizes
+        // allow it: 256 x 256 (8 waves; half the operand bytes per flop of the
+        // 128 tile, measured fastest on the 768-class shapes), else 256 x 128;
+        // otherwise the group's square tile.  MUON_BX_TILE=128 keeps the square
+        // tile and MUON_BX_TILE=256128 asks for 256 x 128 (for tuning sweeps).
+        int bx_tm = grp.tile, bx_tn = grp.tile;
+        if (grp.tile == 128) {
             static const int want = [] {
                 const char* e = getenv("MUON_BX_TILE");
                 return e ? atoi(e) : 0;
             }();
-            if (want == 256) {
-                bool okay = true;
-                for (const Chunk& c : grp.chunks) okay = okay && c.plan.mp % 256 == 0 && c.plan.np % 256 == 0;
-                if (okay) bx_tile = 256;
+            bool rows256 = true, cols256 = true;
+            for (const Chunk& c : grp.chunks) {
+                rows256 = rows256 && c.plan.mp % 256 == 0;
+                cols256 = cols256 && c.plan.np % 256 == 0;
+            }
+            if (want != 128 && want != 256128 && rows256 && cols256) {
+                bx_tm = bx_tn = 256;
+            } else if (want != 128 && rows256) {
+                bx_tm = 256;
+                bx_tn = 128;
             }
         }
         int cur = 0;
@@ -341,7 +351,7 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g3.P = b.B; g3.p_mat = ae; g3.ldp = pl.lda;
                 g3.Q = b.X[cur]; g3.q_mat = xe; g3.ldq = pl.ldx;  // NN: X read as is
                 g3.kpad = static_cast<int>(round_up(pl.m, 64));
-                const int btm = pl.mp / bx_tile, btn = pl.np / bx_tile;
+                const int btm = pl.mp / bx_tm, btn = pl.np / bx_tn;
                 g3.tiles = btm; g3.tiles_n = btn; g3.tiles_per_mat = btm * btn;
                 g3.band = band_rows(btm);
                 g3.E = b.X[cur]; g3.e_mat = xe; g3.lde = pl.ldx;
@@ -350,16 +360,16 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
             }
-            hipError_t e = launch_gemm(GEMM_SYRK, grp.tile, syrk, nb_sym, nullptr, stream);
+            hipError_t e = launch_gemm(GEMM_SYRK, grp.tile, grp.tile, syrk, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
-            e = launch_gemm(GEMM_AAB, grp.tile, aab, nb_sym, nullptr, stream);
+            e = launch_gemm(GEMM_AAB, grp.tile, grp.tile, aab, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");
             const bool timed = sink && !last && sink->recorded < sink->pairs;
             if (timed) {
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded]), stream);
                 if (e != hipSuccess) return hip_fail(e, "event record");
             }
-            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, bx_tile, bx, nb_bx, last ? &out_all : nullptr, stream);
+            e = launch_gemm(last ? GEMM_BX_FINAL : GEMM_BX, bx_tm, bx_tn, bx, nb_bx, last ? &out_all : nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "a X + B X launch");
             if (timed) {
                 e = hipEventRecord(static_cast<hipEvent_t>(sink->events[2 * sink->recorded + 1]), stream);

@@ -15,9 +15,10 @@
 // fragments are formed with gfx950's transposing LDS reads
 // (ds_read_b64_tr_b16), so X is never stored transposed.
 //
-// Engine (gfx950): 256 threads = 4 wavefronts of 64 lanes in a 2x2
-// arrangement, each wave owning a (BM/2)x(BN/2) sub-tile built from 32x32
-// MFMA fragments (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  K advances
+// Engine (gfx950): WGM x WGN wavefronts of 64 lanes (2x2 for square tiles;
+// 4x2 for the 256x128 tile of a X + B X), each owning a (BM/WGM)x(BN/WGN)
+// sub-tile built from 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation).  K advances
 // BK at a time through a ring of STAGES LDS buffers filled by direct
 // global->LDS loads (global_load_lds_dwordx4: each lane supplies a global
 // address, the 64 lanes' 16-byte pieces land contiguously in LDS), so the
@@ -116,13 +117,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int STAGES, int KIND>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrTable out) {
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KIND>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
-    static_assert(!SYM || BM == BN, "symmetric products use square tiles");
+    static_assert(!SYM || (BM == BN && WGM == WGN), "symmetric products use square tiles and wave grids");
     static_assert(BK == 64 || BK == 32, "BK is 32 or 64");
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
-    constexpr int WTM = BM / 2, WTN = BN / 2;  // wave sub-tile
+    constexpr int NW = WGM * WGN;              // wavefronts per workgroup
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave sub-tile
     constexpr int FM = WTM / 32, FN = WTN / 32;
     // a X + B X reads its second operand, X, in its own row-major layout ("NN"):
     // the Q tile is BK rows of K by BN columns, and the MFMA fragments (8
@@ -132,11 +134,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     constexpr int RPI = 64 / CPR;          // rows filled by one wave-wide 1 KB load
     constexpr int CPRQ = NN ? BN / 8 : CPR;  // the same for the Q tile
     constexpr int RPIQ = 64 / CPRQ;
-    constexpr int IP = BM / RPI / 4;       // loads per wave per stage, P operand
-    constexpr int IQ = NN ? BK / RPIQ / 4 : BN / RPI / 4;  // and Q operand
+    constexpr int IP = BM / RPI / NW;      // loads per wave per stage, P operand
+    constexpr int IQ = NN ? BK / RPIQ / NW : BN / RPI / NW;  // and Q operand
     constexpr int NLOAD = IP + IQ;
     constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
-    static_assert(IP >= 1 && IQ >= 1 && RPIQ >= 1, "tile shape not supported by the loader");
+    static_assert(IP >= 1 && IQ >= 1 && RPIQ >= 1 && IP * RPI * NW == BM &&
+                      IQ * NW * (NN ? RPIQ : RPI) == (NN ? BK : BN),
+                  "tile shape not supported by the loader");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-tiles are made of 32 x 32 fragments");
     static_assert(BM * BN <= STAGES * STAGE, "the epilogue reuses the stages as four wave sub-tiles");
 
     __shared__ __attribute__((aligned(1024))) bf16_t lds[STAGES * STAGE];
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     // ---- loader: load i of this wave fills rows r0 = (wave*IP + i)*RPI ..
     // r0 + RPI - 1 of its operand; lane l covers row r0 + l / CPR and LDS slot
@@ -261,11 +266,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
 
     // The epilogue's second operand (AAB: A[j][i] = A[i][j]; BX: old X[i][j])
     // is the K slice [i0, i0 + BM) of the Q operand, which passes through LDS
-    // during the K loop: for tiles up to 128 each wave copies its values out of
-    // the stage of the matching K step, so they are never read from memory
-    // again (for 256 tiles the copies would not fit in registers).  K steps
-    // past kpad hold only padding, whose values are zero.
-    constexpr bool CAPTURE_E = (NN || KIND == GEMM_AAB) && BM <= 128;
+    // during the K loop: for wave sub-tiles up to 64 x 64 each wave copies
+    // its values out of the stage of the matching K step, so they are never
+    // read from memory again (larger sub-tiles' copies would not fit in
+    // registers).  K steps past kpad hold only padding, whose values are zero.
+    constexpr bool CAPTURE_E = (NN || KIND == GEMM_AAB) && FM * FN <= 4;
     u32x2 ev[CAPTURE_E ? FM : 1][CAPTURE_E ? FN : 1][4];
     if constexpr (CAPTURE_E) {
 #pragma unroll
@@ -393,6 +398,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     // drain the loads of the clamped tail steps before the epilogue
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // The epilogue's second operand for sub-tiles too large to capture: the
+    // BM x BN tile of E at (i0, j0), row-major (old X; for b A + c A A the
+    // symmetric A in place of its transpose), is brought into the LDS stages,
+    // which the K loop no longer needs, with 16-byte global->LDS loads laid
+    // out like an NN Q tile; each lane then takes its runs of 4 rows of one
+    // column with transposing reads.
+    constexpr bool STAGE_E = (NN || KIND == GEMM_AAB) && !CAPTURE_E;
+    constexpr int CPRE = BN / 8, RPIE = 64 / CPRE, IE = BM / (RPIE > 0 ? RPIE : 1) / NW;
+    if constexpr (STAGE_E) {
+        static_assert(RPIE >= 1 && IE >= 1 && IE * RPIE * NW == BM, "E tile shape not supported by the loader");
+        __syncthreads();  // every wave is done reading the stages
+        const bf16_t* Et = args.E + static_cast<int64_t>(mat) * args.e_mat + static_cast<int64_t>(i0) * args.lde + j0;
+        const int lre = lane / CPRE, lse = lane % CPRE;
+#pragma unroll
+        for (int i = 0; i < IE; ++i) {
+            const int row = (wave * IE + i) * RPIE + lre;
+            __builtin_amdgcn_global_load_lds(
+                (global_cptr)(Et + static_cast<int64_t>(row) * args.lde + ((lse ^ swq<CPRE>(row)) << 3)),
+                (lds_ptr)(lds + (wave * IE + i) * RPIE * BN), 16, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
     // ---- epilogue.  Accumulator register r of a 32x32 fragment holds, in
     // lane l, row 8*(r/4) + 4*(l/32) + r%4 and column l%32: each lane owns
     // runs of 4 consecutive rows in one column.  The fused update is applied
@@ -408,6 +437,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int j = j0w + fn * 32 + (lane & 31);
+            u32x2 es[4];
+            if constexpr (STAGE_E) {
+                const int ec = wn * WTN + fn * 32 + tq_col;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int er = wm * WTM + fm * 32 + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
+                    es[g4] = lds_read_tr4(lds + er * BN + (((ec >> 3) ^ swq<CPRE>(er)) << 3) + (ec & 7));
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(es[0]), "+v"(es[1]), "+v"(es[2]), "+v"(es[3]));
+            }
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int ib = i0w + fm * 32 + 8 * g4 + 4 * (lane >> 5);
@@ -420,6 +459,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
                     if constexpr (CAPTURE_E) {
                         if constexpr (NN) lgkm_wait_tie(ev[fm][fn][g4]);  // captured by asm reads
                         e4 = ev[fm][fn][g4];
+                    } else if constexpr (STAGE_E) {
+                        e4 = es[g4];
                     } else if constexpr (NN) {
                         // old X[ib..ib+3][j], row-major: 2-byte loads (the 32 lanes
                         // of a half-wave read 64 contiguous bytes of one row)
@@ -571,26 +612,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(GemmLaunch launch, PtrT
     }
 }
 
-template <int BM, int BN, int BK, int STAGES>
+template <int BM, int BN, int BK, int STAGES, int WGM = 2, int WGN = 2>
 hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTable* out, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(blocks));
+    constexpr int NT = 64 * WGM * WGN;
     PtrTable o{};
     if (out) o = *out;
+    if constexpr (BM == BN && WGM == WGN) {
+        switch (kind) {
+            case GEMM_SYRK:
+                k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_SYRK><<<grid, NT, 0, stream>>>(L, o);
+                return hipGetLastError();
+            case GEMM_AAB:
+                k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_AAB><<<grid, NT, 0, stream>>>(L, o);
+                return hipGetLastError();
+            default: break;
+        }
+    }
     switch (kind) {
-        case GEMM_SYRK: k_gemm_nt<BM, BM, BK, STAGES, GEMM_SYRK><<<grid, kThreads, 0, stream>>>(L, o); break;
-        case GEMM_AAB: k_gemm_nt<BM, BM, BK, STAGES, GEMM_AAB><<<grid, kThreads, 0, stream>>>(L, o); break;
-        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX><<<grid, kThreads, 0, stream>>>(L, o); break;
+        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX><<<grid, NT, 0, stream>>>(L, o); break;
         case GEMM_BX_FINAL:
-            k_gemm_nt<BM, BN, BK, STAGES, GEMM_BX_FINAL><<<grid, kThreads, 0, stream>>>(L, o);
+            k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX_FINAL><<<grid, NT, 0, stream>>>(L, o);
             break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
-                       hipStream_t stream) {
+hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& launch, int blocks,
+                       const PtrTable* out, hipStream_t stream) {
+    // 256 x 128 tiles of a X + B X: 8 waves (4 x 2, each 64 x 64), BK 64,
+    // three stages (144 KB of LDS, one workgroup per CU)
+    if (tile == 256 && tile_n == 128) {
+        if (kind != GEMM_BX && kind != GEMM_BX_FINAL) return hipErrorInvalidValue;
+        return launch_t<256, 128, 64, 3, 4, 2>(kind, launch, blocks, out, stream);
+    }
+    if (tile_n != tile) return hipErrorInvalidValue;
+    // 256 x 256 tiles of a X + B X: 8 waves (2 x 4, each 128 x 64) by default,
+    // two per SIMD; MUON_BX_WAVES=4 selects the 4-wave engine (for tuning)
+    static const int bx_waves = [] {
+        const char* s = getenv("MUON_BX_WAVES");
+        return (s && atoi(s) == 4) ? 4 : 8;
+    }();
+    if (tile == 256 && bx_waves == 8 && (kind == GEMM_BX || kind == GEMM_BX_FINAL))
+        return launch_t<256, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
     // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages,
     // 2 = BK 32 with 2 stages for tiles up to 128 (half the LDS, so more
     // workgroups per CU) (MUON_GEMM_PIPE in the environment, for tuning)

@@ -98,7 +98,9 @@ hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int
 // out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream);
 
-hipError_t launch_gemm(GemmKind kind, int tile, const GemmLaunch& launch, int blocks, const PtrTable* out,
-                       hipStream_t stream);
+// One GEMM launch of `blocks` workgroups with tile x tile_n output tiles:
+// square tiles of 64, 128 or 256 for every kind, and 256 x 128 for a X + B X.
+hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& launch, int blocks,
+                       const PtrTable* out, hipStream_t stream);
 
 }  // namespace muon
