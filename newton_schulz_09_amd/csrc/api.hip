@@ -360,6 +360,14 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
             }
+            // the symmetric products' K differs between segments (X X^T: n);
+            // deal whole matrices over the XCDs when the tile counts agree
+            {
+                int tpm = syrk.seg[0].tiles_per_mat;
+                for (int ci = 1; ci < nseg; ++ci)
+                    if (syrk.seg[ci].tiles_per_mat != tpm) tpm = 0;
+                syrk.interleave_tpm = aab.interleave_tpm = tpm;
+            }
             hipError_t e = launch_gemm(GEMM_SYRK, grp.tile, grp.tile, syrk, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
             e = launch_gemm(GEMM_AAB, grp.tile, grp.tile, aab, nb_sym, nullptr, stream);

@@ -67,6 +67,17 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
     return x * q + (x < r ? x : r) + b / kXcds;
 }
 
+// Workgroup b of G -> logical index when every matrix has tpm tiles: XCD x
+// takes whole matrices x, x + 8, x + 16, ... (its tiles of one matrix in
+// order), so segments of different K are spread evenly over the XCDs.  The
+// matrices past the last multiple of 8 keep the dispatch order.
+__device__ __forceinline__ int xcd_interleave(int b, int G, int tpm) {
+    const int full = (G / tpm) / kXcds * kXcds * tpm;  // workgroups of whole rounds of 8 matrices
+    if (b >= full) return b;
+    const int x = b % kXcds, i = b / kXcds;
+    return ((i / tpm) * kXcds + x) * tpm + i % tpm;
+}
+
 // Slot permutation of row r for CPR 16-byte chunks per row (8 or 4).
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
@@ -147,7 +158,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     __shared__ __attribute__((aligned(1024))) bf16_t lds[STAGES * STAGE];
 
     // ---- which segment, which matrix and which output tile
-    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int lid = launch.interleave_tpm > 0
+                        ? xcd_interleave(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x),
+                                         launch.interleave_tpm)
+                        : xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     int si = 0;
 #pragma unroll
     for (int q = 1; q < kMaxSeg; ++q)

@@ -78,6 +78,10 @@ struct GemmArgs {
 struct GemmLaunch {
     GemmArgs seg[kMaxSeg];
     int nseg;
+    // > 0: every segment has this many tiles per matrix, and whole matrices
+    // are dealt round-robin over the XCDs (balances segments whose K
+    // differs); 0: each XCD takes one contiguous range of the grid
+    int interleave_tpm;
 };
 
 hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, float mu,
