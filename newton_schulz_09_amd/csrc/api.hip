@@ -86,6 +86,27 @@ int band_rows(int tiles_m) {
 
 // A dispatch's grid (workgroups x 256 work-items) must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t{1} << 32) / kThreads - 1;
+// Cast workgroups per launch: beyond this each casts several tiles.
+// MUON_CAST_WG_CAP=n lowers the cap (read at every call; for tests of the
+// several-tiles path, which only very large inputs reach otherwise).
+// 64 x 64 tiles per cast workgroup (MUON_CAST_TILES=n, for tuning sweeps):
+// one norm reduction serves them all, and each next tile is loaded while
+// the current one is converted.
+int cast_tiles_per_wg() {
+    static const int n = [] {
+        const char* s = getenv("MUON_CAST_TILES");
+        const int v = s ? atoi(s) : 4;
+        return (v >= 1 && v <= 64) ? v : 4;
+    }();
+    return n;
+}
+
+int64_t max_cast_workgroups() {
+    const char* s = getenv("MUON_CAST_WG_CAP");
+    const long long v = s ? atoll(s) : 0;
+    const int64_t cap = int64_t{1} << 20;
+    return (v >= 1 && v < cap) ? v : cap;
+}
 
 }  // namespace
 
@@ -253,33 +274,81 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 for (int i = 0; i < grp.chunks[ci].plan.cnt; ++i) out_all.p[k++] = grp.chunks[ci].out[i];
             }
         }
+        // the norm pass over every chunk (fused with the momentum in the Muon
+        // step: bf16(u) is staged in X[1], which step 1 overwrites later),
+        // then the bf16 cast into X[0], one launch each
+        ConstPtrTable g_all{};
+        PtrTable b_all{};
+        const bool fused = grp.chunks[0].buf != nullptr;  // the same for every chunk of a call
+        NormLaunch nl{};
+        CastLaunch cl{};
+        nl.nseg = cl.nseg = nseg;
+        int nb_norm = 0, nb_cast = 0;
+        int64_t cast_tiles = 0;
+        for (const Chunk& c : grp.chunks) {
+            const int rows_pad = c.plan.tall ? c.plan.np : c.plan.mp;
+            const int cols_pad = c.plan.tall ? c.plan.mp : c.plan.np;
+            cast_tiles += static_cast<int64_t>(rows_pad / 64) * (cols_pad / 64) * c.plan.cnt;
+        }
+        // tiles per cast workgroup: cast_tiles_per_wg(), more if the grid
+        // would be too large
+        const int64_t cast_cap = max_cast_workgroups();
+        int per_wg = static_cast<int>((cast_tiles + cast_cap - 1) / cast_cap);
+        if (per_wg < cast_tiles_per_wg()) per_wg = cast_tiles_per_wg();
         for (int ci = 0; ci < nseg; ++ci) {
             const Chunk& c = grp.chunks[ci];
             const Ns5Plan& pl = c.plan;
             ChunkBufs b = bufs_of(ws, c);
-            ConstPtrTable gt{};
-            for (int i = 0; i < pl.cnt; ++i) gt.p[i] = c.G[i];
-            // fused Muon step: momentum, norm partials and bf16(u) in one pass;
-            // bf16(u) is staged in X[1], which step 1 overwrites later
-            bf16_t* ub = nullptr;
-            const int64_t ub_mat = static_cast<int64_t>(pl.x_elems);
-            hipError_t e;
-            if (c.buf) {
-                PtrTable bt{};
-                for (int i = 0; i < pl.cnt; ++i) bt.p[i] = c.buf[i];
-                ub = b.X[1];
-                e = launch_momentum_norm(gt, bt, pl.cnt, pl.rows * pl.cols, pl.nb, mu, ub, ub_mat, b.part, stream);
-                if (e != hipSuccess) return hip_fail(e, "momentum + norm launch");
-            } else {
-                e = launch_sumsq(gt, pl.cnt, pl.rows * pl.cols, pl.nb, b.part, stream);
-                if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
+            bool vec = (pl.rows * pl.cols) % 4 == 0;
+            for (int i = 0; i < pl.cnt; ++i) {
+                g_all.p[out_base[ci] + i] = c.G[i];
+                if (fused) b_all.p[out_base[ci] + i] = c.buf[i];
+                vec = vec && (reinterpret_cast<uintptr_t>(c.G[i]) & 15u) == 0 &&
+                      (!fused || (reinterpret_cast<uintptr_t>(c.buf[i]) & 15u) == 0);
             }
-            e = launch_scale_cast(gt, ub, ub_mat, pl.cnt, pl, b.part, eps, b.X[0], stream);
-            if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
-            if (steps == 0) {
+            NormSeg& ns = nl.seg[ci];
+            ns.first_block = nb_norm;
+            ns.nb = pl.nb;
+            ns.ptr_base = out_base[ci];
+            ns.vec = vec ? 1 : 0;
+            ns.numel = pl.rows * pl.cols;
+            ns.chunk = (ns.numel + pl.nb - 1) / pl.nb;
+            if (vec) ns.chunk = (ns.chunk + 3) / 4 * 4;
+            ns.ub = fused ? b.X[1] : nullptr;
+            ns.ub_mat = static_cast<int64_t>(pl.x_elems);
+            ns.partials = b.part;
+            nb_norm += pl.nb * pl.cnt;
+            CastSeg& cs = cl.seg[ci];
+            const int rows_pad = pl.tall ? pl.np : pl.mp;
+            const int cols_pad = pl.tall ? pl.mp : pl.np;
+            cs.first_block = nb_cast;
+            cs.tiles_c = cols_pad / 64;
+            cs.tiles_per_mat = (rows_pad / 64) * cs.tiles_c;
+            cs.per_wg = per_wg;
+            cs.wg_per_mat = (cs.tiles_per_mat + per_wg - 1) / per_wg;
+            cs.ptr_base = out_base[ci];
+            cs.rows = static_cast<int>(pl.rows);
+            cs.cols = static_cast<int>(pl.cols);
+            cs.tall = pl.tall ? 1 : 0;
+            cs.nb = pl.nb;
+            cs.ldx = pl.ldx;
+            cs.ub = fused ? b.X[1] : nullptr;
+            cs.ub_mat = static_cast<int64_t>(pl.x_elems);
+            cs.partials = b.part;
+            cs.X = b.X[0];
+            cs.x_mat = static_cast<int64_t>(pl.x_elems);
+            nb_cast += cs.wg_per_mat * pl.cnt;
+        }
+        hipError_t e = launch_norm(nl, nb_norm, g_all, fused ? &b_all : nullptr, mu, stream);
+        if (e != hipSuccess) return hip_fail(e, fused ? "momentum + norm launch" : "norm (sum of squares) launch");
+        e = launch_scale_cast(cl, nb_cast, g_all, fused, eps, stream);
+        if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
+        if (steps == 0) {
+            for (int ci = 0; ci < nseg; ++ci) {
+                const Chunk& c = grp.chunks[ci];
                 PtrTable ot{};
-                for (int i = 0; i < pl.cnt; ++i) ot.p[i] = c.out[i];
-                e = launch_copy_out(pl, pl.cnt, b.X[0], ot, stream);
+                for (int i = 0; i < c.plan.cnt; ++i) ot.p[i] = c.out[i];
+                e = launch_copy_out(c.plan, c.plan.cnt, bufs_of(ws, c).X[0], ot, stream);
                 if (e != hipSuccess) return hip_fail(e, "copy-out launch");
             }
         }
@@ -368,7 +437,7 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                     if (syrk.seg[ci].tiles_per_mat != tpm) tpm = 0;
                 syrk.interleave_tpm = aab.interleave_tpm = tpm;
             }
-            hipError_t e = launch_gemm(GEMM_SYRK, grp.tile, grp.tile, syrk, nb_sym, nullptr, stream);
+            e = launch_gemm(GEMM_SYRK, grp.tile, grp.tile, syrk, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
             e = launch_gemm(GEMM_AAB, grp.tile, grp.tile, aab, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");

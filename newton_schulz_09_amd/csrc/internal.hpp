@@ -87,17 +87,56 @@ struct GemmLaunch {
 hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, float mu,
                            hipStream_t stream);
 
-hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, double* partials,
-                        hipStream_t stream);
+// One chunk of a batched norm pass: workgroups [first_block, first_block +
+// cnt * nb) of the launch; matrix i of the chunk is entry ptr_base + i of the
+// launch's pointer tables.
+struct NormSeg {
+    int first_block;
+    int nb;        // workgroups (float64 partial sums) per matrix
+    int ptr_base;
+    int vec;       // 16-byte accesses: pointers aligned, numel and chunk multiples of 4
+    int64_t numel; // elements per matrix
+    int64_t chunk; // elements per workgroup
+    bf16_t* ub;    // momentum pass: bf16(u) staging copy, ub_mat elements per matrix
+    int64_t ub_mat;
+    double* partials;
+};
+struct NormLaunch {
+    NormSeg seg[kMaxSeg];
+    int nseg;
+};
 
-// Writes X0 into X (the transpose of G when G is tall).  ub (if non-null):
-// dense bf16 copies of the inputs (stride ub_mat per matrix) to cast from
-// instead of the float32 G.
-hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
-                             const double* partials, float eps, bf16_t* X, hipStream_t stream);
+// Sum of squares of G (BUF null), or Nesterov momentum fused with it (buf
+// updated, bf16(u) staged in ub): one launch over every chunk.
+hipError_t launch_norm(const NormLaunch& L, int blocks, const ConstPtrTable& G, const PtrTable* BUF, float mu,
+                       hipStream_t stream);
 
-hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int cnt, int64_t numel, int nb,
-                                float mu, bf16_t* ub, int64_t ub_mat, double* partials, hipStream_t stream);
+// One chunk of a batched cast: X0 = bf16(bf16(G) / (||G|| + eps)) into X (the
+// transpose of G when G is tall), over X's padded extent.  Each workgroup
+// casts `per_wg` consecutive 64 x 64 tiles of one matrix.
+struct CastSeg {
+    int first_block;
+    int tiles_c;        // tile columns of G's padded extent
+    int tiles_per_mat;
+    int wg_per_mat;     // ceil(tiles_per_mat / per_wg)
+    int per_wg;
+    int ptr_base;
+    int rows, cols, tall, nb, ldx;
+    const bf16_t* ub;   // bf16(G) staging copy (bf16 input), ub_mat elements per matrix
+    int64_t ub_mat;
+    const double* partials;
+    bf16_t* X;
+    int64_t x_mat;
+};
+struct CastLaunch {
+    CastSeg seg[kMaxSeg];
+    int nseg;
+};
+
+// bf16_in: cast from the staging copies (every chunk has one); else from the
+// float32 G of the pointer table.
+hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTable& G, bool bf16_in, float eps,
+                             hipStream_t stream);
 
 // out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream);

@@ -1,15 +1,17 @@
 // Frobenius norm and bf16 cast of the NS5 input (the printed
 // zeroth_power_via_newtonschulz5 of the Muon section, Synced report on
 // Modded-NanoGPT: X = G.bfloat16() / (G.norm() + eps), transposed when G has
-// more rows than columns).
+// more rows than columns), and the Nesterov momentum that precedes it in the
+// Muon step.
 //
-// Two passes, both HBM-bound (in the fused Muon step the first is
-// k_momentum_norm, which also applies the momentum and stages bf16(u)):
-//   k_sumsq      reads G once (4 B/elem) and writes one float64 partial sum
+// Two passes, both HBM-bound, each one launch over every chunk of a launch
+// group (segment tables in the kernel arguments, like the GEMMs):
+//   k_norm       reads G once (4 B/elem) and writes one float64 partial sum
 //                of squares per workgroup: per-lane float64 accumulation,
 //                wavefront butterfly shuffles, then LDS across the 4 waves.
 //                The split of G into workgroups is fixed, so the result is
-//                deterministic (no atomics).
+//                deterministic (no atomics).  In the fused Muon step it also
+//                applies the momentum and stages bf16(u) (14 B/elem).
 //   k_scale_cast reduces a matrix's partials in a fixed order (every
 //                workgroup gets the same float64 norm), then reads G again
 //                (or its bf16 staging copy) and writes
@@ -30,65 +32,54 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void k_sumsq(ConstPtrTable G, int64_t numel, int nb,
-                                                    int64_t chunk, double* partials) {
-    const int mat = blockIdx.y;
-    const float* g = G.p[mat];
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    const int64_t end = begin + chunk < numel ? begin + chunk : numel;
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    int64_t i = begin + threadIdx.x;
-    for (; i + 3 * kThreads < end; i += 4 * kThreads) {
-        const float x0 = g[i], x1 = g[i + kThreads], x2 = g[i + 2 * kThreads], x3 = g[i + 3 * kThreads];
-        s0 = fma(static_cast<double>(x0), static_cast<double>(x0), s0);
-        s1 = fma(static_cast<double>(x1), static_cast<double>(x1), s1);
-        s2 = fma(static_cast<double>(x2), static_cast<double>(x2), s2);
-        s3 = fma(static_cast<double>(x3), static_cast<double>(x3), s3);
-    }
-    for (; i < end; i += kThreads) {
-        const float x = g[i];
-        s0 = fma(static_cast<double>(x), static_cast<double>(x), s0);
-    }
-    double s = wave_sum((s0 + s1) + (s2 + s3));
-    __shared__ double red[kThreads / 64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        partials[static_cast<int64_t>(mat) * nb + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-    }
+// Workgroup b of a batched launch -> its segment (the last one whose first
+// workgroup is at or before b).
+template <typename Launch>
+__device__ __forceinline__ int segment_of(const Launch& L, int b) {
+    int si = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxSeg; ++q)
+        if (q < L.nseg && b >= L.seg[q].first_block) si = q;
+    return si;
 }
 
-// Nesterov momentum fused with the first pass of the norm: one workgroup per
-// contiguous chunk of one matrix reads g and buf, writes the new buf, writes
-// u rounded to bf16 (the bf16(G) of the cast) into a dense staging copy, and
-// leaves one float64 partial sum of squares of the float32 u.  u itself is
-// never stored in float32.  VEC: 16-byte accesses (pointers 16-byte aligned,
-// numel and chunk multiples of 4).
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void k_momentum_norm(ConstPtrTable G, PtrTable BUF, int64_t numel, int nb,
-                                                            int64_t chunk, float mu, bf16_t* ub, int64_t ub_mat,
-                                                            double* partials) {
-    const int mat = blockIdx.y;
-    const float* g = G.p[mat];
-    float* buf = BUF.p[mat];
-    bf16_t* u16 = ub + static_cast<int64_t>(mat) * ub_mat;
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    const int64_t end = begin + chunk < numel ? begin + chunk : numel;
+// MOM = false: sum of squares of G.  MOM = true: Nesterov momentum fused with
+// the first pass of the norm: buf <- mu buf + g, u = g + mu buf; buf is
+// written back, u rounded to bf16 (the bf16(G) of the cast) goes to a dense
+// staging copy, and only u's float64 sum of squares is kept (u itself is
+// never stored in float32).  One workgroup per contiguous chunk of one
+// matrix, one float64 partial per workgroup: the split is fixed, so the norm
+// is deterministic (no atomics).
+template <bool MOM>
+__global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G, PtrTable BUF, float mu) {
+    const NormSeg& sg = L.seg[segment_of(L, static_cast<int>(blockIdx.x))];
+    const int local = static_cast<int>(blockIdx.x) - sg.first_block;
+    const int mat = local / sg.nb, part = local - mat * sg.nb;
+    const float* g = G.p[sg.ptr_base + mat];
+    float* buf = MOM ? BUF.p[sg.ptr_base + mat] : nullptr;
+    bf16_t* u16 = MOM ? sg.ub + static_cast<int64_t>(mat) * sg.ub_mat : nullptr;
+    const int64_t begin = static_cast<int64_t>(part) * sg.chunk;
+    const int64_t end = begin + sg.chunk < sg.numel ? begin + sg.chunk : sg.numel;
     double s0 = 0.0, s1 = 0.0;
-    if constexpr (VEC) {
+    if (sg.vec) {
         for (int64_t i = begin + 4 * static_cast<int64_t>(threadIdx.x); i < end; i += 4 * kThreads) {
             const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
-            f32x4 bv = *reinterpret_cast<const f32x4*>(buf + i);
             float u[4];
+            if constexpr (MOM) {
+                f32x4 bv = *reinterpret_cast<const f32x4*>(buf + i);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bv[q] = fmaf(mu, bv[q], gv[q]);
-                u[q] = fmaf(mu, bv[q], gv[q]);
+                for (int q = 0; q < 4; ++q) {
+                    bv[q] = fmaf(mu, bv[q], gv[q]);
+                    u[q] = fmaf(mu, bv[q], gv[q]);
+                }
+                *reinterpret_cast<f32x4*>(buf + i) = bv;
+                typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<u32x2v*>(u16 + i) =
+                    u32x2v{f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3])};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) u[q] = gv[q];
             }
-            *reinterpret_cast<f32x4*>(buf + i) = bv;
-            typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2v*>(u16 + i) = u32x2v{f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3])};
             s0 = fma(static_cast<double>(u[0]), static_cast<double>(u[0]), s0);
             s1 = fma(static_cast<double>(u[1]), static_cast<double>(u[1]), s1);
             s0 = fma(static_cast<double>(u[2]), static_cast<double>(u[2]), s0);
@@ -96,10 +87,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum_norm(ConstPtrTable G, Ptr
         }
     } else {
         for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
-            const float b = fmaf(mu, buf[i], g[i]);
-            const float u = fmaf(mu, b, g[i]);
-            buf[i] = b;
-            u16[i] = f32_to_bf16(u);
+            float u = g[i];
+            if constexpr (MOM) {
+                const float b = fmaf(mu, buf[i], u);
+                u = fmaf(mu, b, u);
+                buf[i] = b;
+                u16[i] = f32_to_bf16(u);
+            }
             s0 = fma(static_cast<double>(u), static_cast<double>(u), s0);
         }
     }
@@ -108,109 +102,165 @@ __global__ __launch_bounds__(kThreads) void k_momentum_norm(ConstPtrTable G, Ptr
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) red[wave] = s;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        partials[static_cast<int64_t>(mat) * nb + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-    }
+    if (threadIdx.x == 0) sg.partials[static_cast<int64_t>(mat) * sg.nb + part] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 constexpr int kCastTile = 64;
 
-// BF16IN: the input is the dense bf16 staging copy written by
-// k_momentum_norm (already bf16(G)); otherwise the float32 G of the table.
-// One workgroup per 64x64 tile of G: each thread handles runs of 8
-// consecutive columns (16-byte accesses where the shape allows), and a tall
-// G's tile is transposed through LDS so that X rows are also written 16
-// bytes at a time.
+// The float32 quotient q (within ~2 ulps of the exact one) cannot be rounded
+// to bf16 directly: it lies within 8 ulps of a bf16 rounding midpoint, or is
+// not a normal float32 (zero excepted).
+__device__ __forceinline__ bool cast_needs_f64(float q) {
+    const uint32_t bits = __float_as_uint(q);
+    const uint32_t mag = bits & 0x7fffffffu;
+    const bool near_mid = ((bits & 0xffffu) - 0x7ff8u) <= 16u;
+    return near_mid || (mag != 0u && mag < 0x01000000u) || mag >= 0x7f800000u;
+}
+
+// One 64 x 64 tile of the cast: this thread's two runs of 8 consecutive
+// columns (rows idx / 8 for idx = tid and tid + 256), as bf16(G) in float.
 template <bool BF16IN>
-__global__ __launch_bounds__(kThreads) void k_scale_cast(ConstPtrTable G, const bf16_t* ub, int64_t ub_mat, int rows,
-                                                         int cols, int tiles_c, const double* partials, int nb,
-                                                         float eps, bf16_t* X, int ldx, int64_t x_mat, int tall) {
+__device__ __forceinline__ void cast_load(const float* g, const bf16_t* u16, int rows, int cols, bool vec, int r0,
+                                          int c0, float (&v)[2][8]) {
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const int mat = blockIdx.y;
-    const int tr_i = blockIdx.x / tiles_c, tc_i = blockIdx.x % tiles_c;
-    const int r0 = tr_i * kCastTile, c0 = tc_i * kCastTile;
-    const float* g = BF16IN ? nullptr : G.p[mat];
-    const bf16_t* u16 = BF16IN ? ub + static_cast<int64_t>(mat) * ub_mat : nullptr;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-    __shared__ double s_norm;
-    __shared__ __attribute__((aligned(16))) bf16_t tile_t[kCastTile][kCastTile + 8];  // [col][row]
-
-    if (wave == 0) {
-        const double* part = partials + static_cast<int64_t>(mat) * nb;
-        double s = 0.0;
-        for (int k = lane; k < nb; k += 64) s += part[k];
-        s = wave_sum(s);
-        if (lane == 0) s_norm = sqrt(s) + static_cast<double>(eps);
-    }
-    __syncthreads();
-    const double d = s_norm;
-    bf16_t* Xm = X + static_cast<int64_t>(mat) * x_mat;
-    // 16-byte loads need every row start aligned: cols a multiple of 8 (bf16)
-    // or 4 (float32), and the base aligned
-    const bool vec = BF16IN ? ((cols & 7) == 0 && (reinterpret_cast<uintptr_t>(u16) & 15u) == 0)
-                            : ((cols & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15u) == 0);
-
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int idx = threadIdx.x + h * kThreads;  // 0 .. 511
-        const int r = idx >> 3, cg = (idx & 7) * 8;  // tile row, first of 8 columns
-        const int gr = r0 + r, gc = c0 + cg;
-        float v[8];
+        const int idx = threadIdx.x + h * kThreads;
+        const int gr = r0 + (idx >> 3), gc = c0 + (idx & 7) * 8;
         if (gr < rows && vec && gc + 8 <= cols) {
             if constexpr (BF16IN) {
                 const u32x4v w = *reinterpret_cast<const u32x4v*>(u16 + static_cast<int64_t>(gr) * cols + gc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[2 * e] = bf16_to_f32(static_cast<bf16_t>(w[e] & 0xffffu));
-                    v[2 * e + 1] = bf16_to_f32(static_cast<bf16_t>(w[e] >> 16));
+                    v[h][2 * e] = bf16_to_f32(static_cast<bf16_t>(w[e] & 0xffffu));
+                    v[h][2 * e + 1] = bf16_to_f32(static_cast<bf16_t>(w[e] >> 16));
                 }
             } else {
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(g + static_cast<int64_t>(gr) * cols + gc);
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(g + static_cast<int64_t>(gr) * cols + gc + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] = bf16_to_f32(f32_to_bf16(lo[e]));
-                    v[4 + e] = bf16_to_f32(f32_to_bf16(hi[e]));
+                    v[h][e] = bf16_to_f32(f32_to_bf16(lo[e]));
+                    v[h][4 + e] = bf16_to_f32(f32_to_bf16(hi[e]));
                 }
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                v[e] = 0.0f;
+                v[h][e] = 0.0f;
                 if (gr < rows && gc + e < cols) {
                     if constexpr (BF16IN)
-                        v[e] = bf16_to_f32(u16[static_cast<int64_t>(gr) * cols + gc + e]);
+                        v[h][e] = bf16_to_f32(u16[static_cast<int64_t>(gr) * cols + gc + e]);
                     else
-                        v[e] = bf16_to_f32(f32_to_bf16(g[static_cast<int64_t>(gr) * cols + gc + e]));
+                        v[h][e] = bf16_to_f32(f32_to_bf16(g[static_cast<int64_t>(gr) * cols + gc + e]));
                 }
             }
         }
-        // X0 = bf16(bf16(G) / d): the quotient in float64, one rounding;
-        // padding stays zero (0 / d = 0)
-        bf16_t hx[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hx[e] = f64_to_bf16(static_cast<double>(v[e]) / d);
-        if (!tall) {
-            u32x4v w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = static_cast<uint32_t>(hx[2 * e]) | (static_cast<uint32_t>(hx[2 * e + 1]) << 16);
-            *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(gr) * ldx + gc) = w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tile_t[cg + e][r] = hx[e];
-        }
     }
-    if (!tall) return;  // uniform across the workgroup
+}
+
+// BF16IN: the input is the dense bf16 staging copy written by the momentum
+// pass (already bf16(G)); otherwise the float32 G of the table.  Each
+// workgroup casts per_wg consecutive 64 x 64 tiles of one matrix of G's
+// padded extent: it reduces the norm from the partials once (every
+// workgroup of a matrix sums them in the same order, so all get the same
+// float64 norm), then loads each next tile while converting the current one.
+// Each thread handles runs of 8 consecutive columns (16-byte accesses where
+// the shape allows); a tall G's tile is transposed through LDS so that X rows
+// are also written 16 bytes at a time.
+template <bool BF16IN>
+__global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrTable G, float eps) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const CastSeg& sg = L.seg[segment_of(L, static_cast<int>(blockIdx.x))];
+    const int local = static_cast<int>(blockIdx.x) - sg.first_block;
+    const int mat = local / sg.wg_per_mat;
+    const int t_begin = (local - mat * sg.wg_per_mat) * sg.per_wg;
+    const int t_end = t_begin + sg.per_wg < sg.tiles_per_mat ? t_begin + sg.per_wg : sg.tiles_per_mat;
+    const float* g = BF16IN ? nullptr : G.p[sg.ptr_base + mat];
+    const bf16_t* u16 = BF16IN ? sg.ub + static_cast<int64_t>(mat) * sg.ub_mat : nullptr;
+    const int rows = sg.rows, cols = sg.cols;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // 16-byte loads need every row start aligned: cols a multiple of 8 (bf16)
+    // or 4 (float32), and the base aligned
+    const bool vec = BF16IN ? ((cols & 7) == 0 && (reinterpret_cast<uintptr_t>(u16) & 15u) == 0)
+                            : ((cols & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15u) == 0);
+    bf16_t* Xm = sg.X + static_cast<int64_t>(mat) * sg.x_mat;
+
+    __shared__ double s_norm;
+    __shared__ __attribute__((aligned(16))) bf16_t tile_t[kCastTile][kCastTile + 8];  // [col][row]
+
+    if (wave == 0) {
+        const double* part = sg.partials + static_cast<int64_t>(mat) * sg.nb;
+        double s = 0.0;
+        for (int k = lane; k < sg.nb; k += 64) s += part[k];
+        s = wave_sum(s);
+        if (lane == 0) s_norm = sqrt(s) + static_cast<double>(eps);
+    }
     __syncthreads();
-    // X = G^T: X row c0 + c holds G column c0 + c; 8 consecutive G rows per thread
+    const double d = s_norm;
+    // X0 = bf16(fl64(v / d)) for each bf16 value v.  Fast path: q = v *
+    // fl32(1/d) in float32 is within ~2 float32 ulps of v / d, so its
+    // hardware round to bf16 is the same unless q lies within a few ulps of a
+    // bf16 rounding midpoint (low 16 bits near 0x8000); those elements, and
+    // any q that is not a normal float32, take the float64 quotient instead.
+    const float r32 = static_cast<float>(1.0 / d);
+    const bool fast_ok = r32 >= 0x1p-126f && r32 <= 0x1.fffffep127f;
+
+    float v[2][8], vn[2][8];
+    cast_load<BF16IN>(g, u16, rows, cols, vec, (t_begin / sg.tiles_c) * kCastTile,
+                      (t_begin % sg.tiles_c) * kCastTile, v);
+    for (int t = t_begin; t < t_end; ++t) {
+        const int r0 = (t / sg.tiles_c) * kCastTile, c0 = (t % sg.tiles_c) * kCastTile;
+        if (t + 1 < t_end)
+            cast_load<BF16IN>(g, u16, rows, cols, vec, ((t + 1) / sg.tiles_c) * kCastTile,
+                              ((t + 1) % sg.tiles_c) * kCastTile, vn);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int idx = threadIdx.x + h * kThreads;
-        const int c = idx >> 3, rg = (idx & 7) * 8;
-        const u32x4v w = *reinterpret_cast<const u32x4v*>(&tile_t[c][rg]);
-        *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(c0 + c) * ldx + r0 + rg) = w;
+        for (int h = 0; h < 2; ++h) {
+            const int idx = threadIdx.x + h * kThreads;
+            const int r = idx >> 3, cg = (idx & 7) * 8;
+            // X0 = bf16(bf16(G) / d) (padding stays zero: 0 / d = 0)
+            u32x4v w;
+            uint32_t slow = fast_ok ? 0u : 0xffu;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = v[h][2 * e] * r32, q1 = v[h][2 * e + 1] * r32;
+                w[e] = f32x2_to_bf16x2(q0, q1);
+                slow |= (cast_needs_f64(q0) ? 1u : 0u) << (2 * e);
+                slow |= (cast_needs_f64(q1) ? 1u : 0u) << (2 * e + 1);
+            }
+            if (slow) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (slow & (1u << e)) {
+                        const uint32_t hx = f64_to_bf16(static_cast<double>(v[h][e]) / d);
+                        const int sh = 16 * (e & 1);
+                        w[e >> 1] = (w[e >> 1] & ~(0xffffu << sh)) | (hx << sh);
+                    }
+                }
+            }
+            if (!sg.tall) {
+                *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(r0 + r) * sg.ldx + c0 + cg) = w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tile_t[cg + e][r] = static_cast<bf16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+        }
+        if (sg.tall) {  // uniform across the workgroup
+            __syncthreads();
+            // X = G^T: X row c0 + c holds G column c0 + c; 8 consecutive G rows per thread
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int idx = threadIdx.x + h * kThreads;
+                const int c = idx >> 3, rg = (idx & 7) * 8;
+                const u32x4v w = *reinterpret_cast<const u32x4v*>(&tile_t[c][rg]);
+                *reinterpret_cast<u32x4v*>(Xm + static_cast<int64_t>(c0 + c) * sg.ldx + r0 + rg) = w;
+            }
+            __syncthreads();  // tile_t is refilled by the next tile
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[h][e] = vn[h][e];
     }
 }
 
@@ -229,47 +279,21 @@ __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, i
 
 }  // namespace
 
-hipError_t launch_sumsq(const ConstPtrTable& G, int cnt, int64_t numel, int nb, double* partials,
-                        hipStream_t stream) {
-    const int64_t chunk = (numel + nb - 1) / nb;
-    k_sumsq<<<dim3(nb, cnt), kThreads, 0, stream>>>(G, numel, nb, chunk, partials);
+hipError_t launch_norm(const NormLaunch& L, int blocks, const ConstPtrTable& G, const PtrTable* BUF, float mu,
+                       hipStream_t stream) {
+    if (BUF)
+        k_norm<true><<<blocks, kThreads, 0, stream>>>(L, G, *BUF, mu);
+    else
+        k_norm<false><<<blocks, kThreads, 0, stream>>>(L, G, PtrTable{}, mu);
     return hipGetLastError();
 }
 
-hipError_t launch_scale_cast(const ConstPtrTable& G, const bf16_t* ub, int64_t ub_mat, int cnt, const Ns5Plan& plan,
-                             const double* partials, float eps, bf16_t* X, hipStream_t stream) {
-    // X is G's orientation unless G is tall (then it is G^T), written over its
-    // padded extent (padding as zeros)
-    const int rows_pad = plan.tall ? plan.np : plan.mp;
-    const int cols_pad = plan.tall ? plan.mp : plan.np;
-    const int tiles_r = rows_pad / kCastTile, tiles_c = cols_pad / kCastTile;
-    const dim3 grid(tiles_r * tiles_c, cnt);
-    if (ub)
-        k_scale_cast<true><<<grid, kThreads, 0, stream>>>(G, ub, ub_mat, static_cast<int>(plan.rows),
-                                                          static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
-                                                          eps, X, plan.ldx, static_cast<int64_t>(plan.x_elems),
-                                                          plan.tall ? 1 : 0);
+hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTable& G, bool bf16_in, float eps,
+                             hipStream_t stream) {
+    if (bf16_in)
+        k_scale_cast<true><<<blocks, kThreads, 0, stream>>>(L, G, eps);
     else
-        k_scale_cast<false><<<grid, kThreads, 0, stream>>>(G, nullptr, 0, static_cast<int>(plan.rows),
-                                                           static_cast<int>(plan.cols), tiles_c, partials, plan.nb,
-                                                           eps, X, plan.ldx, static_cast<int64_t>(plan.x_elems),
-                                                           plan.tall ? 1 : 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_momentum_norm(const ConstPtrTable& G, const PtrTable& BUF, int cnt, int64_t numel, int nb,
-                                float mu, bf16_t* ub, int64_t ub_mat, double* partials, hipStream_t stream) {
-    bool vec = (numel % 4) == 0;
-    for (int i = 0; i < cnt && vec; ++i)
-        vec = ((reinterpret_cast<uintptr_t>(G.p[i]) | reinterpret_cast<uintptr_t>(BUF.p[i])) & 15u) == 0;
-    int64_t chunk = (numel + nb - 1) / nb;
-    if (vec) chunk = (chunk + 3) / 4 * 4;
-    if (vec)
-        k_momentum_norm<true><<<dim3(nb, cnt), kThreads, 0, stream>>>(G, BUF, numel, nb, chunk, mu, ub, ub_mat,
-                                                                       partials);
-    else
-        k_momentum_norm<false><<<dim3(nb, cnt), kThreads, 0, stream>>>(G, BUF, numel, nb, chunk, mu, ub, ub_mat,
-                                                                        partials);
+        k_scale_cast<false><<<blocks, kThreads, 0, stream>>>(L, G, eps);
     return hipGetLastError();
 }
 

@@ -226,6 +226,31 @@ def test_batched_zero_steps_and_aliasing(muon):
 
 
 
+@pytest.mark.parametrize("cap", [1, 7, 100])
+def test_cast_several_tiles_per_workgroup(muon, monkeypatch, cap):
+    """Very large inputs make each cast workgroup handle several 64x64 tiles of
+    one matrix; a low cap (MUON_CAST_WG_CAP) forces that path here.  X0, the
+    NS5 result and the fused step's outputs and buffers are bitwise those of
+    the one-tile path, for wide, tall, ragged and tile-aligned shapes."""
+    shapes = [(200, 520), (520, 200), (64, 128), (3, 5), (768, 768), (130, 65)]
+    rng = np.random.default_rng(31)
+    Gs = [cuda(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    b0 = [cuda((0.1 * rng.standard_normal(s)).astype(np.float32)) for s in shapes]
+
+    def run():
+        bufs = [b.clone() for b in b0]
+        return (muon.ns5_batched(Gs, steps=0), muon.ns5_batched(Gs),
+                muon.ns5_batched(Gs, bufs=bufs), bufs)
+
+    want = run()
+    monkeypatch.setenv("MUON_CAST_WG_CAP", str(cap))
+    got = run()
+    torch.cuda.synchronize()
+    for part, (w_list, g_list) in zip(("X0", "NS5", "fused", "buffers"), zip(want, got)):
+        for k, (w, g) in enumerate(zip(w_list, g_list)):
+            assert torch.equal(w, g), f"{part} of matrix {k} {shapes[k]} differs with cap {cap}"
+
+
 # ---------------------------------------------------------------- fused Muon step
 
 def test_fused_step_matches_momentum_then_ns5(muon):
