@@ -366,12 +366,16 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 const char* e = getenv("MUON_BX_TILE");
                 return e ? atoi(e) : 0;
             }();
-            bool rows256 = true, cols256 = true;
+            bool rows256 = true, cols256 = true, rows192 = true;
             for (const Chunk& c : grp.chunks) {
                 rows256 = rows256 && c.plan.mp % 256 == 0;
                 cols256 = cols256 && c.plan.np % 256 == 0;
+                rows192 = rows192 && c.plan.mp % 192 == 0;
             }
-            if (want != 128 && want != 256128 && rows256 && cols256) {
+            if (want == 192256 && rows192 && cols256) {
+                bx_tm = 192;
+                bx_tn = 256;
+            } else if (want != 128 && want != 256128 && rows256 && cols256) {
                 bx_tm = bx_tn = 256;
             } else if (want != 128 && rows256) {
                 bx_tm = 256;

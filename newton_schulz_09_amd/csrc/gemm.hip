@@ -45,6 +45,8 @@
 // from memory once).
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace muon {
@@ -94,6 +96,15 @@ __device__ __forceinline__ int swq(int r) {
 }
 
 
+// Slot of 16-byte chunk c in a row of N chunks of an epilogue staging tile,
+// keyed on the row: XOR for power-of-two N, a rotation otherwise (both
+// permute the row's chunks).
+template <int N>
+__device__ __forceinline__ int eslot(int c, int key) {
+    if constexpr ((N & (N - 1)) == 0) return c ^ (key & (N - 1));
+    else return (c + key) % N;
+}
+
 // ds_read_b64_tr_b16: in every group of 16 lanes, lane r supplies the LDS
 // address of 4 consecutive 16-bit values (row r of a 16 x 4 block R); lane i
 // receives R[4e + i/4][i%4] for e = 0..3.  With lane r pointing at
@@ -109,6 +120,16 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const bf16_t* p) {
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)(p)));
     uint64_t v;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// 8-byte LDS read, as inline asm for the same reason (used while
+// global->LDS loads are in flight).
+__device__ __forceinline__ u32x2 lds_read8(const bf16_t* p) {
+    const uint32_t a = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)(p)));
+    uint64_t v;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
     return __builtin_bit_cast(u32x2, v);
 }
 
@@ -351,8 +372,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
                 __builtin_amdgcn_sched_barrier(0);
-                acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][q / FN], b[c][q % FN],
-                                                                              acc[q / FN][q % FN], 0, 0, 0);
+                // NN: Q as the MFMA's first operand, so that the accumulator
+                // is the fragment transposed: each lane holds 4 consecutive
+                // columns of one output row (contiguous in X)
+                if constexpr (NN)
+                    acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[c][q % FN], a[c][q / FN],
+                                                                                  acc[q / FN][q % FN], 0, 0, 0);
+                else
+                    acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][q / FN], b[c][q % FN],
+                                                                                  acc[q / FN][q % FN], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 if (kk + 1 < NKK) {
 #pragma unroll
@@ -386,13 +414,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn) {
                         if constexpr (NN) {
-                            // X rows kin + 8 g4 + 4 (l/32) .. +3 at column (l % 32) of
-                            // this fragment: one transposing read per g4
-                            const int col = wn * WTN + fn * 32 + tq_col;
+                            // X row kin + (l % 32), columns 8 g4 + 4 (l/32) .. +3 of
+                            // this fragment: one 8-byte read per g4
+                            const int krow = kin + (lane & 31);
 #pragma unroll
                             for (int g4 = 0; g4 < 4; ++g4) {
-                                const int krow = kin + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
-                                ev[fm][fn][g4] = lds_read_tr4(
+                                const int col = wn * WTN + fn * 32 + 8 * g4 + 4 * (lane >> 5);
+                                ev[fm][fn][g4] = lds_read8(
                                     sQs + krow * BN + (((col >> 3) ^ swq<CPRQ>(krow)) << 3) + (col & 7));
                             }
                         } else {
@@ -420,6 +448,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     // column with transposing reads.
     constexpr bool STAGE_E = (NN || KIND == GEMM_AAB) && !CAPTURE_E;
     constexpr int CPRE = BN / 8, RPIE = 64 / CPRE, IE = BM / (RPIE > 0 ? RPIE : 1) / NW;
+    // chunk permutation of the staged rows: NN lanes read 32 consecutive rows
+    // at one column (keyed on the whole row); the transposing reads of the
+    // symmetric product read runs of 4 rows (the Q-tile permutation)
+    auto swe = [](int row) { return NN ? (row & (CPRE - 1)) : swq<CPRE>(row); };
     if constexpr (STAGE_E) {
         static_assert(RPIE >= 1 && IE >= 1 && IE * RPIE * NW == BM, "E tile shape not supported by the loader");
         __syncthreads();  // every wave is done reading the stages
@@ -429,7 +461,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
         for (int i = 0; i < IE; ++i) {
             const int row = (wave * IE + i) * RPIE + lre;
             __builtin_amdgcn_global_load_lds(
-                (global_cptr)(Et + static_cast<int64_t>(row) * args.lde + ((lse ^ swq<CPRE>(row)) << 3)),
+                (global_cptr)(Et + static_cast<int64_t>(row) * args.lde + ((lse ^ swe(row)) << 3)),
                 (lds_ptr)(lds + (wave * IE + i) * RPIE * BN), 16, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -438,52 +470,55 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 
     // ---- epilogue.  Accumulator register r of a 32x32 fragment holds, in
     // lane l, row 8*(r/4) + 4*(l/32) + r%4 and column l%32: each lane owns
-    // runs of 4 consecutive rows in one column.  The fused update is applied
-    // in registers and rounded once to bf16; then every wave passes its
+    // runs of 4 consecutive rows in one column.  For NN (operands swapped in
+    // the MFMA) rows and columns trade places: each lane owns runs of 4
+    // consecutive columns of one row.  The fused update is applied in
+    // registers and rounded once to bf16; then every wave passes its
     // (WTM x WTN) sub-tile through its own LDS region to store whole rows with
     // 16-byte stores: as is, and for the symmetric products also transposed
     // into the mirror block.
     const int64_t cm = static_cast<int64_t>(mat);
     const int i0w = i0 + wm * WTM, j0w = j0 + wn * WTN;  // this wave's sub-tile origin
-    u32x2 hv[FM][FN][4];                                  // 4 bf16 (rows ib..ib+3, column j)
+    // 4 bf16: rows ib..ib+3 of column j (NN: columns of row i)
+    u32x2 hv[FM][FN][4];
+    constexpr bool HAS_E = KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL;
+    static_assert(!HAS_E || CAPTURE_E || STAGE_E, "the epilogue operand is captured or staged");
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int j = j0w + fn * 32 + (lane & 31);
             u32x2 es[4];
-            if constexpr (STAGE_E) {
+            if constexpr (STAGE_E && NN) {
+                // row wm*WTM + fm*32 + (l % 32) of the staged tile, columns
+                // 8 g4 + 4 (l / 32) .. +3 of the fragment
+                const int er = wm * WTM + fm * 32 + (lane & 31);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ec = wn * WTN + fn * 32 + 8 * g4 + 4 * (lane >> 5);
+                    es[g4] = *reinterpret_cast<const u32x2*>(lds + er * BN + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
+                }
+            } else if constexpr (STAGE_E) {
                 const int ec = wn * WTN + fn * 32 + tq_col;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int er = wm * WTM + fm * 32 + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
-                    es[g4] = lds_read_tr4(lds + er * BN + (((ec >> 3) ^ swq<CPRE>(er)) << 3) + (ec & 7));
+                    es[g4] = lds_read_tr4(lds + er * BN + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(es[0]), "+v"(es[1]), "+v"(es[2]), "+v"(es[3]));
             }
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int ib = i0w + fm * 32 + 8 * g4 + 4 * (lane >> 5);
                 float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
                 float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
-                if constexpr (KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL) {
-                    // AAB: A[i][j] = A[j][i] (symmetric); BX: old X[i][j] =
-                    // X^T[j][i].  Either way a contiguous run of 4 along i.
+                if constexpr (HAS_E) {
+                    // AAB: A[i..i+3][j] = A[j][i..i+3] (symmetric); BX: old
+                    // X[i][j..j+3].  Either way the run of 4 this lane owns.
                     u32x2 e4;
                     if constexpr (CAPTURE_E) {
                         if constexpr (NN) lgkm_wait_tie(ev[fm][fn][g4]);  // captured by asm reads
                         e4 = ev[fm][fn][g4];
-                    } else if constexpr (STAGE_E) {
-                        e4 = es[g4];
-                    } else if constexpr (NN) {
-                        // old X[ib..ib+3][j], row-major: 2-byte loads (the 32 lanes
-                        // of a half-wave read 64 contiguous bytes of one row)
-                        const bf16_t* e = args.E + cm * args.e_mat + static_cast<int64_t>(ib) * args.lde + j;
-                        e4.x = static_cast<uint32_t>(e[0]) | (static_cast<uint32_t>(e[args.lde]) << 16);
-                        e4.y = static_cast<uint32_t>(e[2 * args.lde]) | (static_cast<uint32_t>(e[3 * args.lde]) << 16);
                     } else {
-                        e4 = *reinterpret_cast<const u32x2*>(args.E + cm * args.e_mat +
-                                                             static_cast<int64_t>(j) * args.lde + ib);
+                        e4 = es[g4];
                     }
                     const float e0 = bf16_to_f32(static_cast<bf16_t>(e4.x & 0xffffu));
                     const float e1 = bf16_to_f32(static_cast<bf16_t>(e4.x >> 16));
@@ -525,7 +560,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int jj = fn * 32 + (lane & 31);
                     const int ii = fm * 32 + 8 * g4 + 4 * (lane >> 5);
-                    *reinterpret_cast<u32x2*>(W + jj * WTM + (((ii >> 3) ^ (jj & (CT_ - 1))) << 3) + (ii & 7)) =
+                    *reinterpret_cast<u32x2*>(W + jj * WTM + (eslot<CT_>(ii >> 3, jj) << 3) + (ii & 7)) =
                         hv[fm][fn][g4];
                 }
     };
@@ -544,16 +579,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                     const int jj = fn * 32 + (lane & 31);
                     const int ib = fm * 32 + 8 * g4 + 4 * (lane >> 5);
                     const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
-                    bf16_t* row0 = W + ib * WTN + (((jj >> 3) ^ ((ib >> 2) & (CN_ - 1))) << 3) + (jj & 7);
+                    bf16_t* row0 = W + ib * WTN + (eslot<CN_>(jj >> 3, ib >> 2) << 3) + (jj & 7);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int ii = ib + q;
                         const bf16_t h = static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
                         if (!sym || ii <= jj) {
                             row0[q * WTN] = h;
-                            if (sym) W[jj * WTN + (((ii >> 3) ^ ((jj >> 2) & (CN_ - 1))) << 3) + (ii & 7)] = h;
+                            if (sym) W[jj * WTN + (eslot<CN_>(ii >> 3, jj >> 2) << 3) + (ii & 7)] = h;
                         }
                     }
+                }
+    };
+    // NN layout (each lane owns row ii, columns jj .. jj+3):
+    // (d) the direct sub-tile [ii][jj], one 8-byte piece per run, chunk
+    // swizzle keyed on the row
+    auto put_rn = [&]() {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ii = fm * 32 + (lane & 31);
+                    const int jj = fn * 32 + 8 * g4 + 4 * (lane >> 5);
+                    *reinterpret_cast<u32x2*>(W + ii * WTN + (eslot<CN_>(jj >> 3, ii) << 3) + (jj & 7)) =
+                        hv[fm][fn][g4];
+                }
+    };
+    // (e) the transposed sub-tile [jj][ii] (2-byte pieces), swizzle keyed on
+    // the row jj as in (a)
+    auto put_tn = [&]() {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ii = fm * 32 + (lane & 31);
+                    const int jj = fn * 32 + 8 * g4 + 4 * (lane >> 5);
+                    const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        W[(jj + q) * WTM + (eslot<CT_>(ii >> 3, jj + q) << 3) + (ii & 7)] =
+                            static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
                 }
     };
     auto lds_fence = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
@@ -561,11 +630,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     // dst with leading dimension ld
     // (`shift` selects the layout's swizzle key: row (transposed) or row / 4
     // (direct))
-    auto store_bf16 = [&](int rows, int cpr, int shift, bf16_t* dst, int ld) {
+    auto store_bf16 = [&](auto cpr_c, int rows, int shift, bf16_t* dst, int ld) {
+        constexpr int cpr = decltype(cpr_c)::value;
         for (int q = lane; q < rows * cpr; q += 64) {
             const int row = q / cpr, c = q % cpr;
             const u32x4 v =
-                *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ ((row >> shift) & (cpr - 1))) << 3));
+                *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + (eslot<cpr>(c, row >> shift) << 3));
             *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(row) * ld + c * 8) = v;
         }
     };
@@ -576,37 +646,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
             // off-diagonal block: the block itself and its mirror
             put_t();
             lds_fence();
-            store_bf16(WTN, CT_, 0, C + static_cast<int64_t>(j0w) * args.ldc + i0w, args.ldc);
+            store_bf16(std::integral_constant<int, CT_>{}, WTN, 0, C + static_cast<int64_t>(j0w) * args.ldc + i0w, args.ldc);
             lds_fence();
             put_n(false);
             lds_fence();
-            store_bf16(WTM, CN_, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+            store_bf16(std::integral_constant<int, CN_>{}, WTM, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
         } else if (wm == wn) {
             // diagonal block: symmetrised once, stored once
             put_n(true);
             lds_fence();
-            store_bf16(WTM, CN_, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+            store_bf16(std::integral_constant<int, CN_>{}, WTM, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
         }
         // (wm > wn on a diagonal tile: the mirror of the wm < wn block)
     } else if constexpr (KIND == GEMM_BX) {
-        put_n(false);
+        put_rn();
         lds_fence();
-        store_bf16(WTM, CN_, 2, args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
+        store_bf16(std::integral_constant<int, CN_>{}, WTM, 0,
+                   args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
     } else {  // GEMM_BX_FINAL: float32 output in G's orientation, clipped to m x n
         float* o = out.p[args.out_base + mat];
         const bool tall = args.tall != 0;
         const int rows = tall ? WTN : WTM, cpr = tall ? CT_ : CN_;
         const int r0 = tall ? j0w : i0w, c0 = tall ? i0w : j0w;   // origin in the output
         const int rlim = tall ? args.n : args.m, clim = tall ? args.m : args.n;  // output rows x cols
-        if (tall) put_t(); else put_n(false);
+        if (tall) put_tn(); else put_rn();  // both keyed on their row
         lds_fence();
         const bool vec_ok = (clim & 3) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
         for (int q = lane; q < rows * cpr; q += 64) {
             const int row = q / cpr, c = q % cpr;
             const int gr = r0 + row, gc = c0 + c * 8;
             if (gr >= rlim || gc >= clim) continue;
-            const int key = tall ? row : (row >> 2);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + ((c ^ (key & (cpr - 1))) << 3));
+            const int slot = tall ? eslot<CT_>(c, row) : eslot<CN_>(c, row);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + (slot << 3));
             float f[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -662,6 +733,12 @@ hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& la
     if (tile == 256 && tile_n == 128) {
         if (kind != GEMM_BX && kind != GEMM_BX_FINAL) return hipErrorInvalidValue;
         return launch_t<256, 128, 64, 3, 4, 2>(kind, launch, blocks, out, stream);
+    }
+    // 192 x 256 tiles of a X + B X: 8 waves (2 x 4, each 96 x 64), BK 64,
+    // two stages (112 KB of LDS)
+    if (tile == 192 && tile_n == 256) {
+        if (kind != GEMM_BX && kind != GEMM_BX_FINAL) return hipErrorInvalidValue;
+        return launch_t<192, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
     }
     if (tile_n != tile) return hipErrorInvalidValue;
     // 256 x 256 tiles of a X + B X: 8 waves (2 x 4, each 128 x 64) by default,
