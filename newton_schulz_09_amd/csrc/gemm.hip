@@ -89,10 +89,12 @@ __device__ __forceinline__ int swz(int r) {
 
 // Slot permutation of row r of a row-major K x N tile (CPRQ chunks per row)
 // read with transposing reads: the 8 rows one read touches (two runs of 4,
-// 8 apart) get distinct offsets.
+// 8 apart) get distinct offsets within one 256-byte bank cycle (rows of 256
+// bytes or more all start on the same bank, so the offsets step by 32 bytes;
+// 128-byte rows alternate halves and step by 16).
 template <int CPRQ>
 __device__ __forceinline__ int swq(int r) {
-    return ((((r & 3) << 1) | ((r >> 3) & 1)) * (CPRQ / 8)) & (CPRQ - 1);
+    return ((((r & 3) << 1) | ((r >> 3) & 1)) * (CPRQ >= 16 ? 2 : 1)) & (CPRQ - 1);
 }
 
 
@@ -593,7 +595,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     };
     // NN layout (each lane owns row ii, columns jj .. jj+3):
     // (d) the direct sub-tile [ii][jj], one 8-byte piece per run, chunk
-    // swizzle keyed on the row
+    // swizzle keyed on ii / 2 (rows pair up in a 256-byte bank cycle, so 16
+    // consecutive rows land on distinct banks)
     auto put_rn = [&]() {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -603,7 +606,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int ii = fm * 32 + (lane & 31);
                     const int jj = fn * 32 + 8 * g4 + 4 * (lane >> 5);
-                    *reinterpret_cast<u32x2*>(W + ii * WTN + (eslot<CN_>(jj >> 3, ii) << 3) + (jj & 7)) =
+                    *reinterpret_cast<u32x2*>(W + ii * WTN + (eslot<CN_>(jj >> 3, ii >> 1) << 3) + (jj & 7)) =
                         hv[fm][fn][g4];
                 }
     };
@@ -628,8 +631,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     auto lds_fence = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
     // (c) store the LDS sub-tile (ROWS rows of CPR chunks) as bf16 rows of
     // dst with leading dimension ld
-    // (`shift` selects the layout's swizzle key: row (transposed) or row / 4
-    // (direct))
+    // (`shift` selects the layout's swizzle key: row (transposed), row / 4
+    // (direct) or row / 2 (NN direct))
     auto store_bf16 = [&](auto cpr_c, int rows, int shift, bf16_t* dst, int ld) {
         constexpr int cpr = decltype(cpr_c)::value;
         for (int q = lane; q < rows * cpr; q += 64) {
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     } else if constexpr (KIND == GEMM_BX) {
         put_rn();
         lds_fence();
-        store_bf16(std::integral_constant<int, CN_>{}, WTM, 0,
+        store_bf16(std::integral_constant<int, CN_>{}, WTM, 1,
                    args.C + cm * args.c_mat + static_cast<int64_t>(i0w) * args.ldc + j0w, args.ldc);
     } else {  // GEMM_BX_FINAL: float32 output in G's orientation, clipped to m x n
         float* o = out.p[args.out_base + mat];
@@ -669,14 +672,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
         const int rows = tall ? WTN : WTM, cpr = tall ? CT_ : CN_;
         const int r0 = tall ? j0w : i0w, c0 = tall ? i0w : j0w;   // origin in the output
         const int rlim = tall ? args.n : args.m, clim = tall ? args.m : args.n;  // output rows x cols
-        if (tall) put_tn(); else put_rn();  // both keyed on their row
+        if (tall) put_tn(); else put_rn();  // keyed on the row / on the row / 2
         lds_fence();
         const bool vec_ok = (clim & 3) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
         for (int q = lane; q < rows * cpr; q += 64) {
             const int row = q / cpr, c = q % cpr;
             const int gr = r0 + row, gc = c0 + c * 8;
             if (gr >= rlim || gc >= clim) continue;
-            const int slot = tall ? eslot<CT_>(c, row) : eslot<CN_>(c, row);
+            const int slot = tall ? eslot<CT_>(c, row) : eslot<CN_>(c, row >> 1);
             const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + (slot << 3));
             float f[8];
 #pragma unroll
