@@ -155,6 +155,26 @@ int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* ro
                      void* stream);
 
 /*
+ * The batched iteration of muon_ns5_batched with caller-chosen coefficients:
+ * each of the `steps` steps is X <- a X + (b A + c A A) X with A = X X^T, in
+ * the same precision, rounding points and layout as NS5.  The Muon section of
+ * the Synced report on Modded-NanoGPT explains its quintic as coefficients
+ * picked for the steepest slope at zero, at the price of converging to a band
+ * around 1 rather than to 1; this entry point also runs the alternatives that
+ * contrast implies, such as the classic cubic Newton-Schulz iteration
+ * (a, b, c) = (1.5, -0.5, 0), whose singular values converge to 1.
+ *  coeffs : host array of 3 floats (a, b, c), each finite.
+ *  Everything else as muon_ns5_batched (same workspace requirement);
+ *  coefficients (MUON_NS5_A, MUON_NS5_B, MUON_NS5_C) give exactly
+ *  muon_ns5_batched's result.
+ * Errors: as muon_ns5_batched, plus MUON_ERR_INVALID_ARG for a null or
+ * non-finite coefficient.
+ */
+int muon_newton_schulz_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                               int64_t count, int steps, const float* coeffs, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * One whole Muon step over a batch: Nesterov momentum (as
  * muon_momentum_nesterov, per matrix) followed by NS5 of the momentum
  * output u (as muon_ns5_batched), with the first pass of the norm fused into

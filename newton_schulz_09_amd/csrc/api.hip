@@ -260,7 +260,14 @@ ChunkBufs bufs_of(char* ws, const Chunk& c) {
 
 // The launch sequence: per chunk the norm and the bf16 cast, then per NS5
 // step one launch per product over every chunk of the group.
-int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps, char* ws, hipStream_t stream,
+// Coefficients (a, b, c) of one iteration step X <- a X + (b A + c A A) X.
+struct Coeffs {
+    float a, b, c;
+};
+constexpr Coeffs kQuintic{MUON_NS5_A, MUON_NS5_B, MUON_NS5_C};
+
+int run_groups(const std::vector<Group>& groups, const Coeffs& k, float mu, int steps, float eps, char* ws,
+               hipStream_t stream,
                EventSink* sink) {
     (void)hipGetLastError();  // start from a clean error state
     for (const Group& grp : groups) {
@@ -415,7 +422,7 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g2.kpad = static_cast<int>(round_up(pl.m, 64));
                 g2.C = b.B; g2.c_mat = ae; g2.ldc = pl.lda;
                 g2.E = b.A; g2.e_mat = ae; g2.lde = pl.lda;
-                g2.alpha = MUON_NS5_B; g2.beta = MUON_NS5_C;
+                g2.alpha = k.b; g2.beta = k.c;
                 nb_sym += g1.tiles_per_mat * pl.cnt;
                 // X' = a X + B X
                 GemmArgs& g3 = bx.seg[ci];
@@ -428,7 +435,7 @@ int run_groups(const std::vector<Group>& groups, float mu, int steps, float eps,
                 g3.tiles = btm; g3.tiles_n = btn; g3.tiles_per_mat = btm * btn;
                 g3.band = band_rows(btm);
                 g3.E = b.X[cur]; g3.e_mat = xe; g3.lde = pl.ldx;
-                g3.alpha = MUON_NS5_A; g3.beta = 1.0f;
+                g3.alpha = k.a; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
@@ -541,7 +548,7 @@ int batched_segments(const float* const* G, float* const* out, float* const* buf
 
 int run_batched(const float* const* G, float* const* out, float* const* buf, float mu, const int64_t* rows,
                 const int64_t* cols, int64_t count, int steps, float eps, void* ws, size_t ws_bytes,
-                hipStream_t stream, EventSink* sink) {
+                hipStream_t stream, EventSink* sink, const Coeffs& k = kQuintic) {
     int st = check_common(steps, eps);
     if (st) return st;
     std::vector<Segment> segs;
@@ -554,7 +561,7 @@ int run_batched(const float* const* G, float* const* out, float* const* buf, flo
     if (st) return st;
     st = check_workspace(ws, ws_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, mu, steps, eps, static_cast<char*>(ws), stream, sink);
+    return run_groups(groups, k, mu, steps, eps, static_cast<char*>(ws), stream, sink);
 }
 
 }  // namespace
@@ -619,8 +626,8 @@ int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, in
     if (st) return st;
     st = check_workspace(workspace, workspace_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, 0.0f, steps, eps, static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
-                      nullptr);
+    return run_groups(groups, kQuintic, 0.0f, steps, eps, static_cast<char*>(workspace),
+                      static_cast<hipStream_t>(stream), nullptr);
 }
 
 int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
@@ -628,6 +635,17 @@ int muon_ns5_batched(const float* const* G, float* const* out, const int64_t* ro
     using namespace muon;
     return run_batched(G, out, nullptr, 0.0f, rows, cols, count, steps, eps, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream), nullptr);
+}
+
+int muon_newton_schulz_batched(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols,
+                               int64_t count, int steps, const float* coeffs, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    if (!coeffs) return fail(MUON_ERR_INVALID_ARG, "null coefficient array");
+    for (int i = 0; i < 3; ++i)
+        if (!isfinite(coeffs[i])) return fail(MUON_ERR_INVALID_ARG, "coefficient %d is not finite", i);
+    return run_batched(G, out, nullptr, 0.0f, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), nullptr, Coeffs{coeffs[0], coeffs[1], coeffs[2]});
 }
 
 int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* const* out, const int64_t* rows,

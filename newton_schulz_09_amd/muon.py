@@ -22,11 +22,16 @@ MUON_ERR_HIP = 4
 
 NS5_STEPS = 5
 NS5_EPS = 1e-7
+#: (a, b, c) of NS5 (MUON_NS5_A/B/C) and of the classic cubic Newton-Schulz
+#: iteration X <- 1.5 X - 0.5 X X^T X, whose singular values converge to 1.
+NS5_COEFFS = (3.4445, -4.7750, 2.0315)
+CUBIC_COEFFS = (1.5, -0.5, 0.0)
 MAX_GROUP = 128
 
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
-           "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_momentum_ns5_batched",
+           "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
+           "muon_momentum_ns5_batched",
            "muon_ns5_batched_timed",
            "muon_status_string", "muon_last_error")
 
@@ -57,6 +62,10 @@ def _load():
     lib.muon_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
                                      ctypes.c_float, vp, sz, vp]
     lib.muon_ns5_batched.restype = ctypes.c_int
+    lib.muon_newton_schulz_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64,
+                                               ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_float, vp,
+                                               sz, vp]
+    lib.muon_newton_schulz_batched.restype = ctypes.c_int
     lib.muon_momentum_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), pi64,
                                               pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.muon_momentum_ns5_batched.restype = ctypes.c_int
@@ -199,7 +208,8 @@ def batched_workspace_size(shapes):
     return int(lib.muon_ns5_batched_workspace_size(rows, cols, n))
 
 
-def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None, bufs=None, mu=0.95):
+def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None, bufs=None, mu=0.95,
+                coeffs=None):
     """NS5 of a list of float32 matrices of any shapes (one device), with one
     launch per product and NS5 step over all matrices that share a tile size.
     Returns the list of outputs (new tensors unless given).
@@ -212,7 +222,12 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
     ``events`` (measurement): a list of ``torch.cuda.Event(enable_timing=True)``
     pairs ``[start0, stop0, start1, stop1, ...]``; the library records them
     around the a X + B X launches of the non-final steps.  The number of
-    pairs recorded is then available as ``ns5_batched.last_recorded``."""
+    pairs recorded is then available as ``ns5_batched.last_recorded``.
+
+    ``coeffs`` (a, b, c): iterate X <- a X + (b A + c A A) X with these
+    coefficients instead of NS5's (muon_newton_schulz_batched), e.g.
+    ``CUBIC_COEFFS`` for the classic cubic Newton-Schulz iteration; not
+    combined with ``bufs`` or ``events``."""
     Gs = list(Gs)
     if not Gs:
         return []
@@ -246,7 +261,15 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
             if b.shape != G.shape or b.device != G.device:
                 raise ValueError(f"bufs[{i}] must have the shape and device of Gs[{i}]")
         b_ptrs = (ctypes.c_void_p * count)(*[b.data_ptr() for b in bufs])
-    if events is None:
+    if coeffs is not None:
+        if b_ptrs is not None or events is not None:
+            raise ValueError("coeffs is not combined with bufs or events")
+        k = tuple(float(c) for c in coeffs)
+        if len(k) != 3:
+            raise ValueError("coeffs must be (a, b, c)")
+        _check(lib.muon_newton_schulz_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), (ctypes.c_float * 3)(*k),
+                                              float(eps), ws.data_ptr(), nbytes, stream))
+    elif events is None:
         if b_ptrs is None:
             _check(lib.muon_ns5_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps), ws.data_ptr(),
                                         nbytes, stream))

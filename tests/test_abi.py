@@ -162,3 +162,23 @@ def test_fused_step_validation_errors_before_any_launch(muon):
     assert b"alias" in lib.muon_last_error()
     assert call(g, b, o, rows, cols, 2, 0.95, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
     assert call(g, b, o, rows, cols, 0, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+
+
+def test_coefficient_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_ns5_batched_workspace_size(rows, cols, 2)
+    call = lib.muon_newton_schulz_batched
+    ok = (ctypes.c_float * 3)(1.5, -0.5, 0.0)
+    assert call(g, o, rows, cols, 2, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"coefficient" in lib.muon_last_error()
+    nan = (ctypes.c_float * 3)(1.5, float("nan"), 0.0)
+    assert call(g, o, rows, cols, 2, 5, nan, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"coefficient 1" in lib.muon_last_error()
+    assert call(g, o, rows, cols, 2, 5, ok, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+    assert call(g, o, rows, cols, 2, -1, ok, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(None, o, rows, cols, 2, 5, ok, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG

@@ -307,3 +307,44 @@ def test_fused_step_misaligned_and_ragged(muon):
         nb, u = oracle.momentum_nesterov(g_host[k], b_host[k], 0.9)
         assert parity.ulp_diff32(parity.to_np(views_b[k]), nb).max() <= 1
         parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(u), f"ragged {shapes[k]}")
+
+
+# ---------------------------------------------------------------- other coefficients
+
+def test_newton_schulz_with_ns5_coefficients_is_ns5(muon):
+    """muon_newton_schulz_batched with NS5's coefficients gives exactly what
+    muon_ns5_batched gives."""
+    rng = np.random.default_rng(41)
+    shapes = [(64, 128), (130, 65), (300, 768), (3, 5)]
+    Gs = [cuda(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    want = muon.ns5_batched(Gs)
+    got = muon.ns5_batched(Gs, coeffs=muon.NS5_COEFFS)
+    torch.cuda.synchronize()
+    for k, (w, g) in enumerate(zip(want, got)):
+        assert torch.equal(w, g), f"matrix {k} {shapes[k]}"
+
+
+@pytest.mark.parametrize("coeffs,steps", [((1.5, -0.5, 0.0), 12), ((2.0, -1.5, 0.5), 3)],
+                         ids=["cubic", "other"])
+def test_newton_schulz_coefficients_parity(muon, coeffs, steps):
+    """Other coefficients meet the parity bar against the oracle run with the
+    same coefficients, for wide, tall and tile-ragged shapes."""
+    rng = np.random.default_rng(43)
+    shapes = [(64, 128), (128, 64), (200, 520), (520, 200), (768, 768)]
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    outs = muon.ns5_batched([cuda(h) for h in host], steps=steps, coeffs=coeffs)
+    torch.cuda.synchronize()
+    for h, o, s in zip(host, outs, shapes):
+        want = oracle.ns5(h, steps=steps, coeffs=coeffs)
+        parity.assert_ns5_parity(parity.to_np(o), want, f"{coeffs} {s}")
+
+
+def test_newton_schulz_identity_coefficients(muon):
+    """(1, 0, 0) leaves the normalised input unchanged, bit for bit."""
+    rng = np.random.default_rng(47)
+    Gs = [cuda(rng.standard_normal(s).astype(np.float32)) for s in [(70, 90), (90, 70), (256, 256)]]
+    want = muon.ns5_batched(Gs, steps=0)
+    got = muon.ns5_batched(Gs, steps=3, coeffs=(1.0, 0.0, 0.0))
+    torch.cuda.synchronize()
+    for w, g in zip(want, got):
+        assert torch.equal(w, g)
