@@ -137,6 +137,31 @@ def muon_step(gs, bufs, mu=0.95, steps=NS5_STEPS, eps=NS5_EPS):
     return new_bufs, outs
 
 
+def apply_update(p, O, lr):
+    """The parameter update that follows the orthogonalisation.  The Muon
+    section's summary paragraph orders the step as momentum, then
+    orthogonalisation, and the update uses the result; its formula did not
+    survive in the page, so the reading is the plain one with a learning
+    rate and no other scaling:
+
+        p <- p - lr * O
+
+    formed in float64 from float32 operands (lr * O is exact there for a
+    bf16-valued O) and rounded once to float32, like the momentum.  Returns
+    the new parameters as float32; inputs are untouched.
+    """
+    p64 = np.asarray(p, dtype=np.float32).astype(np.float64)
+    O64 = np.asarray(O, dtype=np.float32).astype(np.float64)
+    return (p64 - f32(lr) * O64).astype(np.float32)
+
+
+def muon_step_apply(gs, bufs, ps, mu=0.95, lr=0.02, steps=NS5_STEPS, eps=NS5_EPS):
+    """The whole Muon step with its update: momentum, NS5 of u, then
+    ``p - lr * NS5(u)``.  Returns ``(new_bufs, new_params)``."""
+    new_bufs, outs = muon_step(gs, bufs, mu=mu, steps=steps, eps=eps)
+    return new_bufs, [apply_update(p, O, lr) for p, O in zip(ps, outs)]
+
+
 def ns5_nominal_flops(rows, cols, steps=NS5_STEPS):
     """Nominal NS5 flop count, 2 flops per multiply-add: per step the products
     X X^T (2 m^2 n), A A (2 m^3) and B X (2 m^2 n), with m <= n."""
