@@ -19,6 +19,8 @@ Printed (one JSON line on stdout):
   momentum       the stand-alone momentum kernel (16 bytes per element) against
                  HBM
   ns5_4096       NS5 of one 4096x4096 matrix (U diag(s) V^T, seed 3)
+  apply_step     the same step with the parameter update p <- p - lr * O
+                 fused into the last epilogue (muon_momentum_ns5_apply_batched)
   cpu_baseline   the CPU oracle on a bounded sample of the same step
 """
 
@@ -171,6 +173,18 @@ def time_momentum(st, steps, torch):
             "bytes": st.momentum_bytes()}
 
 
+def time_apply_step(st, steps, torch, lr=0.02):
+    st.apply_step(lr)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        st.apply_step(lr)
+    stop.record()
+    torch.cuda.synchronize()
+    return {"ms": round(start.elapsed_time(stop) / steps, 4), "lr": lr}
+
+
 def time_square(torch, muon, workloads, reps=10):
     G, _, _, _ = workloads.square_4096()
     g = torch.from_numpy(G).cuda()
@@ -271,6 +285,8 @@ def main():
         log(f"dominant kernel: {res['roofline']}")
         res["momentum"] = time_momentum(st, args.steps, torch)
         log(f"momentum: {res['momentum']}")
+        res["apply_step"] = time_apply_step(st, args.steps, torch)
+        log(f"apply step: {res['apply_step']}")
         if not args.skip_square:
             res["ns5_4096"] = time_square(torch, muon, workloads)
             log(f"ns5 4096: {res['ns5_4096']}")

@@ -199,6 +199,28 @@ int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* c
                               size_t workspace_bytes, void* stream);
 
 /*
+ * The Muon step with its parameter update: as muon_momentum_ns5_batched, then
+ * p <- p - lr * O with the orthogonalised O, applied in the epilogue of the
+ * last iteration step, so O itself is never stored.  The Muon section of the
+ * Synced report on Modded-NanoGPT orders the step as momentum,
+ * orthogonalisation, update; its update formula did not survive, and this is
+ * the plain reading: a learning rate and no other scaling, with one float32
+ * rounding (fused multiply-add).  A momentum warmup, which the page lists
+ * among the speedrun's techniques, is a schedule of mu over calls.
+ *  p    : host array of `count` device pointers, the float32 parameters
+ *         (rows[i] x cols[i]), read and overwritten; p[i] must not alias g[i]
+ *         or buf[i].
+ *  lr   : learning rate, finite.
+ *  Everything else as muon_momentum_ns5_batched (same workspace
+ *  requirement).
+ * Errors: as muon_momentum_ns5_batched (with p in place of out), plus
+ * MUON_ERR_INVALID_ARG for a null p array, p[i] == g[i] or a non-finite lr.
+ */
+int muon_momentum_ns5_apply_batched(const float* const* g, float* const* buf, float* const* p, const int64_t* rows,
+                                    const int64_t* cols, int64_t count, float mu, float lr, int steps, float eps,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement support: muon_ns5_batched (buf == NULL) or
  * muon_momentum_ns5_batched (buf != NULL, with coefficient mu), which in
  * addition records caller-created hipEvent_t pairs on `stream` around the

@@ -266,8 +266,15 @@ struct Coeffs {
 };
 constexpr Coeffs kQuintic{MUON_NS5_A, MUON_NS5_B, MUON_NS5_C};
 
-int run_groups(const std::vector<Group>& groups, const Coeffs& k, float mu, int steps, float eps, char* ws,
-               hipStream_t stream,
+// What the last step does with O: write it to the outputs, or (apply) update
+// the parameters held there, p <- p - lr * O.
+struct Update {
+    bool apply = false;
+    float lr = 0.0f;
+};
+
+int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& up, float mu, int steps, float eps,
+               char* ws, hipStream_t stream,
                EventSink* sink) {
     (void)hipGetLastError();  // start from a clean error state
     for (const Group& grp : groups) {
@@ -355,7 +362,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, float mu, int 
                 const Chunk& c = grp.chunks[ci];
                 PtrTable ot{};
                 for (int i = 0; i < c.plan.cnt; ++i) ot.p[i] = c.out[i];
-                e = launch_copy_out(c.plan, c.plan.cnt, bufs_of(ws, c).X[0], ot, stream);
+                e = launch_copy_out(c.plan, c.plan.cnt, bufs_of(ws, c).X[0], ot, stream, up.apply, up.lr);
                 if (e != hipSuccess) return hip_fail(e, "copy-out launch");
             }
         }
@@ -438,6 +445,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, float mu, int 
                 g3.alpha = k.a; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
+                g3.apply = up.apply ? 1 : 0; g3.lr = up.lr;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
             }
             // the symmetric products' K differs between segments (X X^T: n);
@@ -548,7 +556,7 @@ int batched_segments(const float* const* G, float* const* out, float* const* buf
 
 int run_batched(const float* const* G, float* const* out, float* const* buf, float mu, const int64_t* rows,
                 const int64_t* cols, int64_t count, int steps, float eps, void* ws, size_t ws_bytes,
-                hipStream_t stream, EventSink* sink, const Coeffs& k = kQuintic) {
+                hipStream_t stream, EventSink* sink, const Coeffs& k = kQuintic, const Update& up = Update{}) {
     int st = check_common(steps, eps);
     if (st) return st;
     std::vector<Segment> segs;
@@ -561,7 +569,7 @@ int run_batched(const float* const* G, float* const* out, float* const* buf, flo
     if (st) return st;
     st = check_workspace(ws, ws_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, k, mu, steps, eps, static_cast<char*>(ws), stream, sink);
+    return run_groups(groups, k, up, mu, steps, eps, static_cast<char*>(ws), stream, sink);
 }
 
 }  // namespace
@@ -626,7 +634,7 @@ int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, in
     if (st) return st;
     st = check_workspace(workspace, workspace_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, kQuintic, 0.0f, steps, eps, static_cast<char*>(workspace),
+    return run_groups(groups, kQuintic, Update{}, 0.0f, steps, eps, static_cast<char*>(workspace),
                       static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -655,6 +663,24 @@ int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* c
     if (!buf) return fail(MUON_ERR_INVALID_ARG, "null momentum buffer array");
     return run_batched(g, out, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream), nullptr);
+}
+
+int muon_momentum_ns5_apply_batched(const float* const* g, float* const* buf, float* const* p, const int64_t* rows,
+                                    const int64_t* cols, int64_t count, float mu, float lr, int steps, float eps,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    if (!buf) return fail(MUON_ERR_INVALID_ARG, "null momentum buffer array");
+    if (!p) return fail(MUON_ERR_INVALID_ARG, "null parameter array");
+    if (!isfinite(lr)) return fail(MUON_ERR_INVALID_ARG, "lr must be finite");
+    if (g && count > 0)
+        for (int64_t i = 0; i < count; ++i)
+            if (p[i] && p[i] == g[i])
+                return fail(MUON_ERR_INVALID_ARG, "parameters must not alias the gradient (index %lld)", (long long)i);
+    Update up;
+    up.apply = true;
+    up.lr = lr;
+    return run_batched(g, p, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), nullptr, kQuintic, up);
 }
 
 int muon_ns5_batched_timed(const float* const* G, float* const* out, float* const* buf, float mu,

@@ -689,12 +689,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
             }
             float* dst = o + static_cast<int64_t>(gr) * clim + gc;
             if (vec_ok && gc + 8 <= clim) {
-                *reinterpret_cast<f32x4*>(dst) = f32x4{f[0], f[1], f[2], f[3]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{f[4], f[5], f[6], f[7]};
+                f32x4 lo = f32x4{f[0], f[1], f[2], f[3]}, hi = f32x4{f[4], f[5], f[6], f[7]};
+                if (args.apply) {  // p - lr * O, one rounding
+                    const f32x4 plo = *reinterpret_cast<const f32x4*>(dst);
+                    const f32x4 phi = *reinterpret_cast<const f32x4*>(dst + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = fmaf(-args.lr, lo[e], plo[e]);
+                        hi[e] = fmaf(-args.lr, hi[e], phi[e]);
+                    }
+                }
+                *reinterpret_cast<f32x4*>(dst) = lo;
+                *reinterpret_cast<f32x4*>(dst + 4) = hi;
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (gc + e < clim) dst[e] = f[e];
+                    if (gc + e < clim) dst[e] = args.apply ? fmaf(-args.lr, f[e], dst[e]) : f[e];
             }
         }
     }

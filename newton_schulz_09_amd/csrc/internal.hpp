@@ -73,6 +73,10 @@ struct GemmArgs {
     int lde;
     float alpha, beta;
     int m, n, tall;
+    // final step: 0 writes O to the output table; 1 updates the parameters
+    // there instead, p <- p - lr * O (one float32 rounding)
+    int apply;
+    float lr;
 };
 
 struct GemmLaunch {
@@ -139,7 +143,9 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
                              hipStream_t stream);
 
 // out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
-hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream);
+// apply: out[i] <- out[i] - lr * X (the parameter update) instead.
+hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
+                           bool apply = false, float lr = 0.0f);
 
 // One GEMM launch of `blocks` workgroups with tile x tile_n output tiles:
 // square tiles of 64, 128 or 256 for every kind, and 256 x 128 for a X + B X.

@@ -264,8 +264,10 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     }
 }
 
+// out[i] = float32 of X in G's orientation (the steps = 0 result), or with
+// `apply` the parameter update out[i] <- out[i] - lr * X.
 __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int tall, int ldx,
-                                                       const bf16_t* X, int64_t x_mat) {
+                                                       const bf16_t* X, int64_t x_mat, int apply, float lr) {
     const int mat = blockIdx.y;
     const int64_t total = static_cast<int64_t>(rows) * cols;
     const bf16_t* src = X + static_cast<int64_t>(mat) * x_mat;
@@ -273,7 +275,8 @@ __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, i
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
         const int64_t r = i / cols, c = i - r * cols;  // position in G's orientation
-        dst[i] = bf16_to_f32(tall ? src[c * ldx + r] : src[r * ldx + c]);
+        const float o = bf16_to_f32(tall ? src[c * ldx + r] : src[r * ldx + c]);
+        dst[i] = apply ? fmaf(-lr, o, dst[i]) : o;
     }
 }
 
@@ -297,13 +300,14 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
     return hipGetLastError();
 }
 
-hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream) {
+hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
+                           bool apply, float lr) {
     const int64_t total = plan.rows * plan.cols;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 2048) blocks = 2048;
     k_copy_out<<<dim3(static_cast<unsigned>(blocks), cnt), kThreads, 0, stream>>>(
         out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), plan.tall ? 1 : 0, plan.ldx, X,
-        static_cast<int64_t>(plan.x_elems));
+        static_cast<int64_t>(plan.x_elems), apply ? 1 : 0, lr);
     return hipGetLastError();
 }
 

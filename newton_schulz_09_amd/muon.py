@@ -31,7 +31,7 @@ MAX_GROUP = 128
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
-           "muon_momentum_ns5_batched",
+           "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
            "muon_ns5_batched_timed",
            "muon_status_string", "muon_last_error")
 
@@ -69,6 +69,10 @@ def _load():
     lib.muon_momentum_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), pi64,
                                               pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.muon_momentum_ns5_batched.restype = ctypes.c_int
+    lib.muon_momentum_ns5_apply_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                    pi64, pi64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                                    ctypes.c_float, vp, sz, vp]
+    lib.muon_momentum_ns5_apply_batched.restype = ctypes.c_int
     lib.muon_ns5_batched_timed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                            ctypes.c_float, pi64, pi64, i64, ctypes.c_int, ctypes.c_float, vp, sz,
                                            vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -209,7 +213,7 @@ def batched_workspace_size(shapes):
 
 
 def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, events=None, bufs=None, mu=0.95,
-                coeffs=None):
+                coeffs=None, lr=None):
     """NS5 of a list of float32 matrices of any shapes (one device), with one
     launch per product and NS5 step over all matrices that share a tile size.
     Returns the list of outputs (new tensors unless given).
@@ -227,7 +231,11 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
     ``coeffs`` (a, b, c): iterate X <- a X + (b A + c A A) X with these
     coefficients instead of NS5's (muon_newton_schulz_batched), e.g.
     ``CUBIC_COEFFS`` for the classic cubic Newton-Schulz iteration; not
-    combined with ``bufs`` or ``events``."""
+    combined with ``bufs`` or ``events``.
+
+    ``lr`` (with ``bufs``): the Muon step with its update
+    (muon_momentum_ns5_apply_batched): ``outs`` are the parameters, updated
+    in place to ``p - lr * NS5(u)``; not combined with ``events``."""
     Gs = list(Gs)
     if not Gs:
         return []
@@ -261,7 +269,12 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
             if b.shape != G.shape or b.device != G.device:
                 raise ValueError(f"bufs[{i}] must have the shape and device of Gs[{i}]")
         b_ptrs = (ctypes.c_void_p * count)(*[b.data_ptr() for b in bufs])
-    if coeffs is not None:
+    if lr is not None:
+        if b_ptrs is None or events is not None or coeffs is not None:
+            raise ValueError("lr needs bufs, and is not combined with events or coeffs")
+        _check(lib.muon_momentum_ns5_apply_batched(g_ptrs, b_ptrs, o_ptrs, rows, cols, count, float(mu), float(lr),
+                                                   int(steps), float(eps), ws.data_ptr(), nbytes, stream))
+    elif coeffs is not None:
         if b_ptrs is not None or events is not None:
             raise ValueError("coeffs is not combined with bufs or events")
         k = tuple(float(c) for c in coeffs)

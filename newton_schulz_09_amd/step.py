@@ -69,6 +69,18 @@ class MuonStep:
                          events=events, bufs=self.bufs, mu=self.mu)
         return self.outs
 
+    def apply_step(self, lr):
+        """The whole step with its parameter update, in one call: the
+        parameters ``params`` (allocated as zeros on first use, one flat
+        float32 buffer laid out like the gradients) become ``p - lr * NS5(u)``;
+        the update O is never stored."""
+        if not hasattr(self, "param"):
+            self.param = torch.zeros(self.total, dtype=torch.float32, device=self.device)
+            self.params = self._views(self.param)
+        muon.ns5_batched(self.grads, self.params, steps=self.steps, eps=self.eps, workspace=self.workspace,
+                         bufs=self.bufs, mu=self.mu, lr=lr)
+        return self.params
+
     def step(self):
         """Enqueue one step on the current stream; results land in ``outs``
         (and the new state in ``bufs``)."""

@@ -182,3 +182,27 @@ def test_coefficient_validation_errors_before_any_launch(muon):
     assert call(g, o, rows, cols, 2, 5, ok, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
     assert call(g, o, rows, cols, 2, -1, ok, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
     assert call(None, o, rows, cols, 2, 5, ok, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+
+
+def test_apply_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    b = (ctypes.c_void_p * 2)(0x400000, 0x400100)
+    p = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_ns5_batched_workspace_size(rows, cols, 2)
+    call = lib.muon_momentum_ns5_apply_batched
+    assert call(g, b, None, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, None, p, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, p, rows, cols, 2, 0.95, float("inf"), 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"lr" in lib.muon_last_error()
+    alias_g = (ctypes.c_void_p * 2)(0x300000, 0x100100)     # p[1] == g[1]
+    assert call(g, b, alias_g, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"gradient" in lib.muon_last_error()
+    alias_b = (ctypes.c_void_p * 2)(0x400000, 0x300100)     # p[0] == buf[0]
+    assert call(g, b, alias_b, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    nullp = (ctypes.c_void_p * 2)(0x300000, 0)
+    assert call(g, b, nullp, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, p, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE

@@ -348,3 +348,40 @@ def test_newton_schulz_identity_coefficients(muon):
     torch.cuda.synchronize()
     for w, g in zip(want, got):
         assert torch.equal(w, g)
+
+
+# ---------------------------------------------------------------- the step with its update
+
+def _apply_reference(p, O, lr):
+    """p - lr*O with one float32 rounding, from the GPU's own O: lr*O is exact
+    in float64 (O is bf16-valued) and so is the difference at these
+    magnitudes, so rounding it to float32 is the fused multiply-add."""
+    return (p.astype(np.float64) - np.float64(np.float32(lr)) * O.astype(np.float64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("steps", [5, 0])
+def test_apply_step_updates_parameters(muon, steps):
+    """muon_momentum_ns5_apply_batched: the buffers are those of the step
+    without the update, and the parameters become p - lr * O with the O that
+    step returns (one float32 rounding); O itself meets the parity bar."""
+    rng = np.random.default_rng(51)
+    shapes = [(64, 128), (128, 64), (200, 520), (520, 200), (3, 5), (768, 768), (33, 17)]
+    gs = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    bs = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    ps = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    lr = 0.02
+    b1 = [cuda(b) for b in bs]
+    outs = muon.ns5_batched([cuda(g) for g in gs], steps=steps, bufs=b1, mu=0.9)
+    b2 = [cuda(b) for b in bs]
+    p2 = [cuda(p) for p in ps]
+    muon.ns5_batched([cuda(g) for g in gs], p2, steps=steps, bufs=b2, mu=0.9, lr=lr)
+    torch.cuda.synchronize()
+    for k, s in enumerate(shapes):
+        assert torch.equal(b1[k], b2[k]), f"buffers {s}"
+        O = parity.to_np(outs[k])
+        want = _apply_reference(ps[k], O, lr)
+        d = parity.ulp_diff32(parity.to_np(p2[k]), want)
+        assert d.max() <= 1 and np.mean(d == 0) >= 0.999, f"update {s}"
+        _, u = oracle.momentum_nesterov(gs[k], bs[k], 0.9)
+        if steps:
+            parity.assert_ns5_parity(O, oracle.ns5(u, steps=steps), f"O {s}")

@@ -64,6 +64,39 @@ def test_gpt2_124m_fused_step_all_matrices(mods):
 
 
 @pytest.mark.timeout(900)
+def test_gpt2_124m_apply_step_all_matrices(mods):
+    """GPT-2 124M set, the step with its parameter update: the buffers equal
+    the fused step's, and every parameter matrix becomes p - lr * O with the
+    fused step's O (one float32 rounding; O meets the parity bar in the test
+    above).  Exercises the update in both orientations of the final epilogue."""
+    _, step_mod = mods
+    items = workloads.gpt2_124m()
+    shapes = [it[2].shape for it in items]
+    runs = []
+    for _ in range(2):
+        st = step_mod.MuonStep(shapes)
+        for k, (_, _, G, buf) in enumerate(items):
+            st.grads[k].copy_(torch.from_numpy(G))
+            st.bufs[k].copy_(torch.from_numpy(buf))
+        runs.append(st)
+    plain, upd = runs
+    plain.fused_step()
+    rng = np.random.default_rng(61)
+    p0 = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    upd.param = torch.from_numpy(np.concatenate([np.pad(p.ravel(), (0, (-p.size) % 64)) for p in p0])).cuda()
+    upd.params = upd._views(upd.param)
+    lr = 0.02
+    upd.apply_step(lr)
+    torch.cuda.synchronize()
+    for k, s in enumerate(shapes):
+        assert torch.equal(plain.bufs[k], upd.bufs[k]), f"buffers {k} {s}"
+        O = parity.to_np(plain.outs[k]).astype(np.float64)
+        want = (p0[k].astype(np.float64) - np.float64(np.float32(lr)) * O).astype(np.float32)
+        d = parity.ulp_diff32(parity.to_np(upd.params[k]), want)
+        assert d.max() <= 1 and np.mean(d == 0) >= 0.999, f"update {k} {s}"
+
+
+@pytest.mark.timeout(900)
 def test_gpt2_124m_step_all_matrices(mods):
     """GPT-2 124M hidden-matrix set: one full step, every matrix checked."""
     _, step_mod = mods
