@@ -175,6 +175,23 @@ int muon_newton_schulz_batched(const float* const* G, float* const* out, const i
                                size_t workspace_bytes, void* stream);
 
 /*
+ * NS5 of bfloat16 matrices, returning bfloat16 (as muon_ns5_batched, whose
+ * inputs and outputs are float32).  The printed listing of the Muon section
+ * (Synced report on Modded-NanoGPT) casts G to bfloat16 before the iteration
+ * and returns the result in G's dtype, so for a bfloat16 G the cast is exact
+ * and the output is the last iterate X itself, transposed back for a tall G,
+ * with no further rounding.  The norm is taken over G's bfloat16 values in
+ * float64, as for float32 inputs.
+ *  G, out : host arrays of `count` device pointers to bfloat16 bit patterns,
+ *           row-major rows[i] x cols[i]; out[i] may alias G[i]; distinct i
+ *           must not overlap.
+ *  Everything else as muon_ns5_batched (same workspace requirement).
+ * Errors: as muon_ns5_batched.
+ */
+int muon_ns5_batched_bf16(const uint16_t* const* G, uint16_t* const* out, const int64_t* rows, const int64_t* cols,
+                          int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One whole Muon step over a batch: Nesterov momentum (as
  * muon_momentum_nesterov, per matrix) followed by NS5 of the momentum
  * output u (as muon_ns5_batched), with the first pass of the norm fused into

@@ -271,6 +271,7 @@ constexpr Coeffs kQuintic{MUON_NS5_A, MUON_NS5_B, MUON_NS5_C};
 struct Update {
     bool apply = false;
     float lr = 0.0f;
+    bool bf16_io = false;  // G and the outputs hold bfloat16 (the outputs get X as is)
 };
 
 int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& up, float mu, int steps, float eps,
@@ -294,6 +295,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
         ConstPtrTable g_all{};
         PtrTable b_all{};
         const bool fused = grp.chunks[0].buf != nullptr;  // the same for every chunk of a call
+        const bool in16 = up.bf16_io;
         NormLaunch nl{};
         CastLaunch cl{};
         nl.nseg = cl.nseg = nseg;
@@ -313,7 +315,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             const Chunk& c = grp.chunks[ci];
             const Ns5Plan& pl = c.plan;
             ChunkBufs b = bufs_of(ws, c);
-            bool vec = (pl.rows * pl.cols) % 4 == 0;
+            bool vec = (pl.rows * pl.cols) % (in16 ? 8 : 4) == 0;
             for (int i = 0; i < pl.cnt; ++i) {
                 g_all.p[out_base[ci] + i] = c.G[i];
                 if (fused) b_all.p[out_base[ci] + i] = c.buf[i];
@@ -327,7 +329,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             ns.vec = vec ? 1 : 0;
             ns.numel = pl.rows * pl.cols;
             ns.chunk = (ns.numel + pl.nb - 1) / pl.nb;
-            if (vec) ns.chunk = (ns.chunk + 3) / 4 * 4;
+            if (vec) ns.chunk = in16 ? (ns.chunk + 7) / 8 * 8 : (ns.chunk + 3) / 4 * 4;
             ns.ub = fused ? b.X[1] : nullptr;
             ns.ub_mat = static_cast<int64_t>(pl.x_elems);
             ns.partials = b.part;
@@ -353,16 +355,17 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             cs.x_mat = static_cast<int64_t>(pl.x_elems);
             nb_cast += cs.wg_per_mat * pl.cnt;
         }
-        hipError_t e = launch_norm(nl, nb_norm, g_all, fused ? &b_all : nullptr, mu, stream);
+        hipError_t e = launch_norm(nl, nb_norm, g_all, fused ? &b_all : nullptr, mu, stream, in16);
         if (e != hipSuccess) return hip_fail(e, fused ? "momentum + norm launch" : "norm (sum of squares) launch");
-        e = launch_scale_cast(cl, nb_cast, g_all, fused, eps, stream);
+        e = launch_scale_cast(cl, nb_cast, g_all, fused || in16, eps, stream);
         if (e != hipSuccess) return hip_fail(e, "scale/cast launch");
         if (steps == 0) {
             for (int ci = 0; ci < nseg; ++ci) {
                 const Chunk& c = grp.chunks[ci];
                 PtrTable ot{};
                 for (int i = 0; i < c.plan.cnt; ++i) ot.p[i] = c.out[i];
-                e = launch_copy_out(c.plan, c.plan.cnt, bufs_of(ws, c).X[0], ot, stream, up.apply, up.lr);
+                e = launch_copy_out(c.plan, c.plan.cnt, bufs_of(ws, c).X[0], ot, stream, up.apply, up.lr,
+                                    up.bf16_io);
                 if (e != hipSuccess) return hip_fail(e, "copy-out launch");
             }
         }
@@ -445,7 +448,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                 g3.alpha = k.a; g3.beta = 1.0f;
                 g3.C = b.X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
                 g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
-                g3.apply = up.apply ? 1 : 0; g3.lr = up.lr;
+                g3.apply = up.apply ? 1 : 0; g3.lr = up.lr; g3.out16 = up.bf16_io ? 1 : 0;
                 nb_bx += g3.tiles_per_mat * pl.cnt;
             }
             // the symmetric products' K differs between segments (X X^T: n);
@@ -663,6 +666,17 @@ int muon_momentum_ns5_batched(const float* const* g, float* const* buf, float* c
     if (!buf) return fail(MUON_ERR_INVALID_ARG, "null momentum buffer array");
     return run_batched(g, out, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream), nullptr);
+}
+
+int muon_ns5_batched_bf16(const uint16_t* const* G, uint16_t* const* out, const int64_t* rows, const int64_t* cols,
+                          int64_t count, int steps, float eps, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    Update up;
+    up.bf16_io = true;
+    // the pointer tables carry addresses only; the kernels read and write bf16
+    return run_batched(reinterpret_cast<const float* const*>(G), reinterpret_cast<float* const*>(out), nullptr,
+                       0.0f, rows, cols, count, steps, eps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), nullptr, kQuintic, up);
 }
 
 int muon_momentum_ns5_apply_batched(const float* const* g, float* const* buf, float* const* p, const int64_t* rows,

@@ -675,12 +675,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
         if (tall) put_tn(); else put_rn();  // keyed on the row / on the row / 2
         lds_fence();
         const bool vec_ok = (clim & 3) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
+        const bool vec16 = (clim & 7) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
         for (int q = lane; q < rows * cpr; q += 64) {
             const int row = q / cpr, c = q % cpr;
             const int gr = r0 + row, gc = c0 + c * 8;
             if (gr >= rlim || gc >= clim) continue;
             const int slot = tall ? eslot<CT_>(c, row) : eslot<CN_>(c, row >> 1);
             const u32x4 v = *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + (slot << 3));
+            if (args.out16) {  // bfloat16 output: X as is
+                bf16_t* d16 = reinterpret_cast<bf16_t*>(o) + static_cast<int64_t>(gr) * clim + gc;
+                if (vec16 && gc + 8 <= clim) {
+                    *reinterpret_cast<u32x4*>(d16) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gc + e < clim) d16[e] = static_cast<bf16_t>((v[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                }
+                continue;
+            }
             float f[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

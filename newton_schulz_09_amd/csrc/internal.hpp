@@ -77,6 +77,7 @@ struct GemmArgs {
     // there instead, p <- p - lr * O (one float32 rounding)
     int apply;
     float lr;
+    int out16;  // final step: the output table holds bfloat16 (X as is)
 };
 
 struct GemmLaunch {
@@ -112,8 +113,9 @@ struct NormLaunch {
 
 // Sum of squares of G (BUF null), or Nesterov momentum fused with it (buf
 // updated, bf16(u) staged in ub): one launch over every chunk.
+// in16: G holds bfloat16 values (sum of squares only).
 hipError_t launch_norm(const NormLaunch& L, int blocks, const ConstPtrTable& G, const PtrTable* BUF, float mu,
-                       hipStream_t stream);
+                       hipStream_t stream, bool in16 = false);
 
 // One chunk of a batched cast: X0 = bf16(bf16(G) / (||G|| + eps)) into X (the
 // transpose of G when G is tall), over X's padded extent.  Each workgroup
@@ -126,7 +128,7 @@ struct CastSeg {
     int per_wg;
     int ptr_base;
     int rows, cols, tall, nb, ldx;
-    const bf16_t* ub;   // bf16(G) staging copy (bf16 input), ub_mat elements per matrix
+    const bf16_t* ub;   // bf16(G) staging copy (bf16 input; null: G itself is bf16), ub_mat elements per matrix
     int64_t ub_mat;
     const double* partials;
     bf16_t* X;
@@ -143,9 +145,10 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
                              hipStream_t stream);
 
 // out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
-// apply: out[i] <- out[i] - lr * X (the parameter update) instead.
+// apply: out[i] <- out[i] - lr * X (the parameter update) instead; out16:
+// out[i] holds bfloat16 and receives X as is.
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
-                           bool apply = false, float lr = 0.0f);
+                           bool apply = false, float lr = 0.0f, bool out16 = false);
 
 // One GEMM launch of `blocks` workgroups with tile x tile_n output tiles:
 // square tiles of 64, 128 or 256 for every kind, and 256 x 128 for a X + B X.

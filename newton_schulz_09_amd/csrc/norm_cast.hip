@@ -50,12 +50,47 @@ __device__ __forceinline__ int segment_of(const Launch& L, int b) {
 // never stored in float32).  One workgroup per contiguous chunk of one
 // matrix, one float64 partial per workgroup: the split is fixed, so the norm
 // is deterministic (no atomics).
-template <bool MOM>
+// IN16: G holds bfloat16 values (the bf16-input NS5; no momentum), read 8
+// at a time where aligned.
+template <bool MOM, bool IN16 = false>
 __global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G, PtrTable BUF, float mu) {
+    static_assert(!(MOM && IN16), "the momentum pass reads float32 gradients");
     const NormSeg& sg = L.seg[segment_of(L, static_cast<int>(blockIdx.x))];
     const int local = static_cast<int>(blockIdx.x) - sg.first_block;
     const int mat = local / sg.nb, part = local - mat * sg.nb;
     const float* g = G.p[sg.ptr_base + mat];
+    if constexpr (IN16) {
+        const bf16_t* h = reinterpret_cast<const bf16_t*>(g);
+        const int64_t begin = static_cast<int64_t>(part) * sg.chunk;
+        const int64_t end = begin + sg.chunk < sg.numel ? begin + sg.chunk : sg.numel;
+        double s0 = 0.0, s1 = 0.0;
+        if (sg.vec) {  // 16-byte aligned, numel and chunk multiples of 8
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            for (int64_t i = begin + 8 * static_cast<int64_t>(threadIdx.x); i < end; i += 8 * kThreads) {
+                const u32x4v w = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(h + i));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const double lo = bf16_to_f32(static_cast<bf16_t>(w[q] & 0xffffu));
+                    const double hi = bf16_to_f32(static_cast<bf16_t>(w[q] >> 16));
+                    s0 = fma(lo, lo, s0);
+                    s1 = fma(hi, hi, s1);
+                }
+            }
+        } else {
+            for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
+                const double v = bf16_to_f32(h[i]);
+                s0 = fma(v, v, s0);
+            }
+        }
+        double s = wave_sum(s0 + s1);
+        __shared__ double red16[kThreads / 64];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) red16[wave] = s;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            sg.partials[static_cast<int64_t>(mat) * sg.nb + part] = (red16[0] + red16[1]) + (red16[2] + red16[3]);
+        return;
+    }
     float* buf = MOM ? BUF.p[sg.ptr_base + mat] : nullptr;
     bf16_t* u16 = MOM ? sg.ub + static_cast<int64_t>(mat) * sg.ub_mat : nullptr;
     const int64_t begin = static_cast<int64_t>(part) * sg.chunk;
@@ -177,7 +212,10 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     const int t_begin = (local - mat * sg.wg_per_mat) * sg.per_wg;
     const int t_end = t_begin + sg.per_wg < sg.tiles_per_mat ? t_begin + sg.per_wg : sg.tiles_per_mat;
     const float* g = BF16IN ? nullptr : G.p[sg.ptr_base + mat];
-    const bf16_t* u16 = BF16IN ? sg.ub + static_cast<int64_t>(mat) * sg.ub_mat : nullptr;
+    // bf16 input: the staging copy, or (bf16-input NS5) G itself
+    const bf16_t* u16 = !BF16IN ? nullptr
+                        : sg.ub ? sg.ub + static_cast<int64_t>(mat) * sg.ub_mat
+                                : reinterpret_cast<const bf16_t*>(G.p[sg.ptr_base + mat]);
     const int rows = sg.rows, cols = sg.cols;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // 16-byte loads need every row start aligned: cols a multiple of 8 (bf16)
@@ -264,10 +302,12 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     }
 }
 
-// out[i] = float32 of X in G's orientation (the steps = 0 result), or with
-// `apply` the parameter update out[i] <- out[i] - lr * X.
+// out[i] = float32 of X in G's orientation (the steps = 0 result), with
+// `apply` the parameter update out[i] <- out[i] - lr * X instead, or with
+// `out16` X itself as bfloat16.
 __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, int cols, int tall, int ldx,
-                                                       const bf16_t* X, int64_t x_mat, int apply, float lr) {
+                                                       const bf16_t* X, int64_t x_mat, int apply, float lr,
+                                                       int out16) {
     const int mat = blockIdx.y;
     const int64_t total = static_cast<int64_t>(rows) * cols;
     const bf16_t* src = X + static_cast<int64_t>(mat) * x_mat;
@@ -275,16 +315,23 @@ __global__ __launch_bounds__(kThreads) void k_copy_out(PtrTable out, int rows, i
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
         const int64_t r = i / cols, c = i - r * cols;  // position in G's orientation
-        const float o = bf16_to_f32(tall ? src[c * ldx + r] : src[r * ldx + c]);
-        dst[i] = apply ? fmaf(-lr, o, dst[i]) : o;
+        const bf16_t x = tall ? src[c * ldx + r] : src[r * ldx + c];
+        if (out16) {
+            reinterpret_cast<bf16_t*>(dst)[i] = x;
+        } else {
+            const float o = bf16_to_f32(x);
+            dst[i] = apply ? fmaf(-lr, o, dst[i]) : o;
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_norm(const NormLaunch& L, int blocks, const ConstPtrTable& G, const PtrTable* BUF, float mu,
-                       hipStream_t stream) {
-    if (BUF)
+                       hipStream_t stream, bool in16) {
+    if (in16)
+        k_norm<false, true><<<blocks, kThreads, 0, stream>>>(L, G, PtrTable{}, mu);
+    else if (BUF)
         k_norm<true><<<blocks, kThreads, 0, stream>>>(L, G, *BUF, mu);
     else
         k_norm<false><<<blocks, kThreads, 0, stream>>>(L, G, PtrTable{}, mu);
@@ -301,13 +348,13 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
 }
 
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
-                           bool apply, float lr) {
+                           bool apply, float lr, bool out16) {
     const int64_t total = plan.rows * plan.cols;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 2048) blocks = 2048;
     k_copy_out<<<dim3(static_cast<unsigned>(blocks), cnt), kThreads, 0, stream>>>(
         out, static_cast<int>(plan.rows), static_cast<int>(plan.cols), plan.tall ? 1 : 0, plan.ldx, X,
-        static_cast<int64_t>(plan.x_elems), apply ? 1 : 0, lr);
+        static_cast<int64_t>(plan.x_elems), apply ? 1 : 0, lr, out16 ? 1 : 0);
     return hipGetLastError();
 }
 

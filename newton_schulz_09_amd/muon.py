@@ -31,7 +31,7 @@ MAX_GROUP = 128
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
-           "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
+           "muon_ns5_batched_bf16", "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
            "muon_ns5_batched_timed",
            "muon_status_string", "muon_last_error")
 
@@ -66,6 +66,9 @@ def _load():
                                                ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_float, vp,
                                                sz, vp]
     lib.muon_newton_schulz_batched.restype = ctypes.c_int
+    lib.muon_ns5_batched_bf16.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64, ctypes.c_int,
+                                          ctypes.c_float, vp, sz, vp]
+    lib.muon_ns5_batched_bf16.restype = ctypes.c_int
     lib.muon_momentum_ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), pi64,
                                               pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.muon_momentum_ns5_batched.restype = ctypes.c_int
@@ -98,13 +101,13 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require_f32_cuda(t, name):
+def _require_f32_cuda(t, name, dtype=torch.float32):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -192,14 +195,14 @@ def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
     return outs
 
 
-def _outputs(Gs, outs):
+def _outputs(Gs, outs, dtype=torch.float32):
     if outs is None:
         return [torch.empty_like(G) for G in Gs]
     outs = list(outs)
     if len(outs) != len(Gs):
         raise ValueError("outs must match Gs in length")
     for i, (G, o) in enumerate(zip(Gs, outs)):
-        _require_f32_cuda(o, f"outs[{i}]")
+        _require_f32_cuda(o, f"outs[{i}]", dtype)
         if o.shape != G.shape or o.device != G.device:
             raise ValueError(f"outs[{i}] must have the shape and device of Gs[{i}]")
     return outs
@@ -235,18 +238,27 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
 
     ``lr`` (with ``bufs``): the Muon step with its update
     (muon_momentum_ns5_apply_batched): ``outs`` are the parameters, updated
-    in place to ``p - lr * NS5(u)``; not combined with ``events``."""
+    in place to ``p - lr * NS5(u)``; not combined with ``events``.
+
+    bfloat16 ``Gs`` (all of them): NS5 returning bfloat16, the last iterate as
+    is (muon_ns5_batched_bf16); only ``outs``, ``steps``, ``eps`` and
+    ``workspace`` apply."""
     Gs = list(Gs)
     if not Gs:
         return []
+    dtype = Gs[0].dtype if isinstance(Gs[0], torch.Tensor) else torch.float32
+    if dtype == torch.bfloat16 and (bufs is not None or events is not None or coeffs is not None or lr is not None):
+        raise ValueError("bfloat16 inputs take only outs, steps, eps and workspace")
+    if dtype != torch.bfloat16:
+        dtype = torch.float32
     for i, G in enumerate(Gs):
-        _require_f32_cuda(G, f"Gs[{i}]")
+        _require_f32_cuda(G, f"Gs[{i}]", dtype)
         if G.dim() != 2:
             raise ValueError(f"Gs[{i}] must be 2-D")
     device = Gs[0].device
     if any(G.device != device for G in Gs):
         raise ValueError("all matrices must be on one device")
-    outs = _outputs(Gs, outs)
+    outs = _outputs(Gs, outs, dtype)
     count = len(Gs)
     shapes = [tuple(G.shape) for G in Gs]
     need = batched_workspace_size(shapes)
@@ -269,7 +281,10 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
             if b.shape != G.shape or b.device != G.device:
                 raise ValueError(f"bufs[{i}] must have the shape and device of Gs[{i}]")
         b_ptrs = (ctypes.c_void_p * count)(*[b.data_ptr() for b in bufs])
-    if lr is not None:
+    if dtype == torch.bfloat16:
+        _check(lib.muon_ns5_batched_bf16(g_ptrs, o_ptrs, rows, cols, count, int(steps), float(eps), ws.data_ptr(),
+                                         nbytes, stream))
+    elif lr is not None:
         if b_ptrs is None or events is not None or coeffs is not None:
             raise ValueError("lr needs bufs, and is not combined with events or coeffs")
         _check(lib.muon_momentum_ns5_apply_batched(g_ptrs, b_ptrs, o_ptrs, rows, cols, count, float(mu), float(lr),

@@ -206,3 +206,19 @@ def test_apply_validation_errors_before_any_launch(muon):
     nullp = (ctypes.c_void_p * 2)(0x300000, 0)
     assert call(g, b, nullp, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
     assert call(g, b, p, rows, cols, 2, 0.95, 0.02, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+
+
+def test_bf16_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_ns5_batched_workspace_size(rows, cols, 2)
+    call = lib.muon_ns5_batched_bf16
+    assert call(None, o, rows, cols, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, None, 2, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, cols, 2, -1, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, cols, 2, 5, float("nan"), ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, cols, 2, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE

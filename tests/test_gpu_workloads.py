@@ -97,6 +97,26 @@ def test_gpt2_124m_apply_step_all_matrices(mods):
 
 
 @pytest.mark.timeout(900)
+def test_gpt2_124m_bf16_inputs(mods):
+    """GPT-2 124M set given as bfloat16: outputs are bfloat16 (the last
+    iterate) and agree with the float32 entry point on the same values, for
+    every matrix and both orientations of the 256-tile final epilogue; sampled
+    matrices meet the parity bar against the oracle."""
+    muon, _ = mods
+    items = workloads.gpt2_124m()
+    host = [oracle.round_bf16(G).astype(np.float32) for (_, _, G, _) in items]
+    out16 = muon.ns5_batched([torch.from_numpy(h).cuda().to(torch.bfloat16) for h in host])
+    out32 = muon.ns5_batched([torch.from_numpy(h).cuda() for h in host])
+    torch.cuda.synchronize()
+    for k, (o16, o32) in enumerate(zip(out16, out32)):
+        assert o16.dtype == torch.bfloat16
+        d = parity.bf16_ulp_diff(o16.float().cpu().numpy(), parity.to_np(o32))
+        assert np.mean(d == 0) >= 0.99, f"matrix {k}: {np.mean(d != 0):.3%} differ"
+    for k in (0, 13, 26, 39):
+        parity.assert_ns5_parity(out16[k].float().cpu().numpy(), oracle.ns5(host[k]), f"bf16 matrix {k}")
+
+
+@pytest.mark.timeout(900)
 def test_gpt2_124m_step_all_matrices(mods):
     """GPT-2 124M hidden-matrix set: one full step, every matrix checked."""
     _, step_mod = mods
