@@ -318,6 +318,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 for (int g4 = 0; g4 < 4; ++g4) ev[fm][fn][g4] = u32x2{0u, 0u};
     }
 
+    // The epilogue's second operand for sub-tiles too large to capture: the
+    // BM x BN tile of E at (i0, j0), row-major (old X; for b A + c A A the
+    // symmetric A in place of its transpose), is brought into LDS stages the
+    // K loop no longer needs, with 16-byte global->LDS loads: rows [0, EH)
+    // during the last K step, into the stage that step would otherwise refill
+    // with a redundant copy, and rows [EH, BM) after the loop into the stage
+    // it read.  Each lane then reads its runs of 4 (NN: 8-byte row pieces;
+    // otherwise transposing reads of 4 rows of one column).
+    // (Pipelines whose stages cannot hold half the tile, and wave sub-tiles
+    // of more than 8 fragments, whose registers are full, load it whole after
+    // the loop, from the base of the LDS.)
+    constexpr bool STAGE_E = (NN || KIND == GEMM_AAB) && !CAPTURE_E;
+    constexpr int CPRE = BN / 8, RPIE = 64 / CPRE, EH = BM / 2;
+    constexpr bool E_SPLIT = STAGE_E && EH * BN <= STAGE && FM * FN <= 8;
+    constexpr int NEH = EH / (RPIE > 0 ? RPIE : 1) / NW;  // loads per wave per half
+    static_assert(!STAGE_E || (RPIE >= 1 && NEH >= 1 && NEH * RPIE * NW == EH),
+                  "E tile shape not supported by the loader");
+    // chunk permutation of the staged rows: NN lanes read 32 consecutive rows
+    // at one column (keyed on the whole row); the transposing reads of the
+    // symmetric product read runs of 4 rows (the Q-tile permutation)
+    auto swe = [](int row) { return NN ? (row & (CPRE - 1)) : swq<CPRE>(row); };
+    const bf16_t* Et = args.E + static_cast<int64_t>(mat) * args.e_mat + static_cast<int64_t>(i0) * args.lde + j0;
+    // load i of half h of this wave's share of the E tile to `dst` (the
+    // half's first row)
+    auto issue_e = [&](int i, int h, bf16_t* dst) {
+        const int lre = lane / CPRE, lse = lane % CPRE;
+        const int rl = (wave * NEH + i) * RPIE + lre;  // row within the half
+        const int row = h * EH + rl;
+        __builtin_amdgcn_global_load_lds(
+            (global_cptr)(Et + static_cast<int64_t>(row) * args.lde + ((lse ^ swe(row)) << 3)),
+            (lds_ptr)(dst + (wave * NEH + i) * RPIE * BN), 16, 0, 0);
+    };
+
     const int nk = args.kpad / BK;
     // Every iteration issues the NLOAD loads of one K step (STAGES-1 steps
     // ahead), so the number of loads outstanding behind step kt is always
@@ -401,11 +434,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 }
                 const int g = kk * NMF + q;
 #pragma unroll
-                for (int L = 0; L < NLOAD; ++L)
-                    if ((L * LWIN) / NLOAD == g) issue_one(L, kl, sl);
+                for (int L = 0; L < NLOAD; ++L) {
+                    if ((L * LWIN) / NLOAD == g) {
+                        if (E_SPLIT && kt == nk - 1) {  // the first half of E instead of a redundant reload
+                            if (L < NEH) issue_e(L, 0, lds + sl * STAGE);
+                        } else {
+                            issue_one(L, kl, sl);
+                        }
+                    }
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (E_SPLIT && NEH > NLOAD) {
+            if (kt == nk - 1)
+                for (int i = NLOAD; i < NEH; ++i) issue_e(i, 0, lds + sl * STAGE);
+        }
         if constexpr (CAPTURE_E) {
             const bf16_t* sQs = lds + (kt % STAGES) * STAGE + BM * BK;
 #pragma unroll
@@ -439,32 +483,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
             }
         }
     }
-    // drain the loads of the clamped tail steps before the epilogue
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // drain the loads of the clamped tail steps before the epilogue (with a
+    // split E tile those are its first half, waited for below)
+    if constexpr (!E_SPLIT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // The epilogue's second operand for sub-tiles too large to capture: the
-    // BM x BN tile of E at (i0, j0), row-major (old X; for b A + c A A the
-    // symmetric A in place of its transpose), is brought into the LDS stages,
-    // which the K loop no longer needs, with 16-byte global->LDS loads laid
-    // out like an NN Q tile; each lane then takes its runs of 4 rows of one
-    // column with transposing reads.
-    constexpr bool STAGE_E = (NN || KIND == GEMM_AAB) && !CAPTURE_E;
-    constexpr int CPRE = BN / 8, RPIE = 64 / CPRE, IE = BM / (RPIE > 0 ? RPIE : 1) / NW;
-    // chunk permutation of the staged rows: NN lanes read 32 consecutive rows
-    // at one column (keyed on the whole row); the transposing reads of the
-    // symmetric product read runs of 4 rows (the Q-tile permutation)
-    auto swe = [](int row) { return NN ? (row & (CPRE - 1)) : swq<CPRE>(row); };
     if constexpr (STAGE_E) {
-        static_assert(RPIE >= 1 && IE >= 1 && IE * RPIE * NW == BM, "E tile shape not supported by the loader");
-        __syncthreads();  // every wave is done reading the stages
-        const bf16_t* Et = args.E + static_cast<int64_t>(mat) * args.e_mat + static_cast<int64_t>(i0) * args.lde + j0;
-        const int lre = lane / CPRE, lse = lane % CPRE;
+        // the second half of the epilogue operand, into the stage the last K
+        // step read (the first half was loaded during that step); or the
+        // whole tile from the LDS base
+        // every wave is done reading the stages (its own LDS reads are
+        // complete; loads still in flight write only the other stage)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < IE; ++i) {
-            const int row = (wave * IE + i) * RPIE + lre;
-            __builtin_amdgcn_global_load_lds(
-                (global_cptr)(Et + static_cast<int64_t>(row) * args.lde + ((lse ^ swe(row)) << 3)),
-                (lds_ptr)(lds + (wave * IE + i) * RPIE * BN), 16, 0, 0);
+        for (int i = 0; i < NEH; ++i) {
+            if constexpr (E_SPLIT) {
+                issue_e(i, 1, lds + ((nk - 1) % STAGES) * STAGE);
+            } else {
+                issue_e(i, 0, lds);
+                issue_e(i, 1, lds + EH * BN);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -490,6 +527,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             u32x2 es[4];
+            // row r of the staged E tile (half r / EH)
+            auto erow = [&](int r) -> const bf16_t* {
+                if constexpr (!E_SPLIT) return lds + r * BN;
+                // the stage the last K step refilled, and the one it read
+                const int st = r < EH ? (nk + STAGES - 2) % STAGES : (nk - 1) % STAGES;
+                return lds + st * STAGE + (r < EH ? r : r - EH) * BN;
+            };
             if constexpr (STAGE_E && NN) {
                 // row wm*WTM + fm*32 + (l % 32) of the staged tile, columns
                 // 8 g4 + 4 (l / 32) .. +3 of the fragment
@@ -497,14 +541,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int ec = wn * WTN + fn * 32 + 8 * g4 + 4 * (lane >> 5);
-                    es[g4] = *reinterpret_cast<const u32x2*>(lds + er * BN + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
+                    es[g4] = *reinterpret_cast<const u32x2*>(erow(er) + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
                 }
             } else if constexpr (STAGE_E) {
                 const int ec = wn * WTN + fn * 32 + tq_col;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int er = wm * WTM + fm * 32 + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
-                    es[g4] = lds_read_tr4(lds + er * BN + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
+                    es[g4] = lds_read_tr4(erow(er) + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(es[0]), "+v"(es[1]), "+v"(es[2]), "+v"(es[3]));
             }
