@@ -399,41 +399,74 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                 bx_tn = 128;
             }
         }
+        // tile of X X^T: 256 (8 waves; half the operand bytes per flop of the
+        // 128 tile) wherever every chunk's padded m allows it, else the
+        // group's (MUON_SYRK_TILE=128 keeps the group's, for tuning sweeps).
+        // Its K (= n) differs between segments, and 256 tiles are few, so
+        // its segments go longest K first: the last workgroups to start are
+        // the shortest.
+        int syrk_tile = grp.tile;
+        {
+            static const int want = [] {
+                const char* e = getenv("MUON_SYRK_TILE");
+                return e ? atoi(e) : 0;
+            }();
+            bool rows256 = true;
+            for (const Chunk& c : grp.chunks) rows256 = rows256 && c.plan.mp % 256 == 0;
+            if (want != 128 && grp.tile == 128 && rows256) syrk_tile = 256;
+        }
+        int syrk_order[kMaxSeg];
+        for (int ci = 0; ci < nseg; ++ci) syrk_order[ci] = ci;
+        for (int a = 1; a < nseg; ++a)  // insertion sort by n, descending (stable)
+            for (int b = a; b > 0 && grp.chunks[syrk_order[b]].plan.n > grp.chunks[syrk_order[b - 1]].plan.n; --b) {
+                const int t = syrk_order[b];
+                syrk_order[b] = syrk_order[b - 1];
+                syrk_order[b - 1] = t;
+            }
         int cur = 0;
         for (int s = 0; s < steps; ++s) {
             const int nxt = cur ^ 1;
             const bool last = (s == steps - 1);
             GemmLaunch syrk{}, aab{}, bx{};
             syrk.nseg = aab.nseg = bx.nseg = nseg;
-            int nb_sym = 0, nb_bx = 0;
-            for (int ci = 0; ci < nseg; ++ci) {
-                const Chunk& c = grp.chunks[ci];
+            int nb_syrk = 0, nb_sym = 0, nb_bx = 0;
+            for (int k = 0; k < nseg; ++k) {  // A = X X^T, longest K first
+                const Chunk& c = grp.chunks[syrk_order[k]];
                 const Ns5Plan& pl = c.plan;
                 ChunkBufs b = bufs_of(ws, c);
-                const int T = pl.tile;
-                const int tiles_m = pl.mp / T;
+                const int tiles_m = pl.mp / syrk_tile;
                 const int64_t xe = static_cast<int64_t>(pl.x_elems);
-                const int64_t ae = static_cast<int64_t>(pl.a_elems);
-                // A = X X^T
-                GemmArgs& g1 = syrk.seg[ci];
-                g1.first_block = nb_sym;
-                g1.out_base = out_base[ci];
+                GemmArgs& g1 = syrk.seg[k];
+                g1.first_block = nb_syrk;
+                g1.out_base = out_base[syrk_order[k]];
                 g1.P = b.X[cur]; g1.p_mat = xe; g1.ldp = pl.ldx;
                 g1.Q = b.X[cur]; g1.q_mat = xe; g1.ldq = pl.ldx;
                 g1.kpad = static_cast<int>(round_up(pl.n, 64));
                 g1.tiles = tiles_m; g1.tiles_n = tiles_m; g1.tiles_per_mat = tiles_m * (tiles_m + 1) / 2;
-                g1.C = b.A; g1.c_mat = ae; g1.ldc = pl.lda;
+                g1.C = b.A; g1.c_mat = static_cast<int64_t>(pl.a_elems); g1.ldc = pl.lda;
                 g1.m = pl.m; g1.n = pl.n; g1.tall = pl.tall ? 1 : 0;
-                // B = b A + c A A  (same triangle of tiles)
+                nb_syrk += g1.tiles_per_mat * pl.cnt;
+            }
+            for (int ci = 0; ci < nseg; ++ci) {
+                const Chunk& c = grp.chunks[ci];
+                const Ns5Plan& pl = c.plan;
+                ChunkBufs b = bufs_of(ws, c);
+                const int tiles_m = pl.mp / pl.tile;
+                const int64_t xe = static_cast<int64_t>(pl.x_elems);
+                const int64_t ae = static_cast<int64_t>(pl.a_elems);
+                // B = b A + c A A  (the upper triangle of tiles)
                 GemmArgs& g2 = aab.seg[ci];
-                g2 = g1;
+                g2.first_block = nb_sym;
+                g2.out_base = out_base[ci];
+                g2.tiles = tiles_m; g2.tiles_n = tiles_m; g2.tiles_per_mat = tiles_m * (tiles_m + 1) / 2;
+                g2.m = pl.m; g2.n = pl.n; g2.tall = pl.tall ? 1 : 0;
                 g2.P = b.A; g2.p_mat = ae; g2.ldp = pl.lda;
                 g2.Q = b.A; g2.q_mat = ae; g2.ldq = pl.lda;
                 g2.kpad = static_cast<int>(round_up(pl.m, 64));
                 g2.C = b.B; g2.c_mat = ae; g2.ldc = pl.lda;
                 g2.E = b.A; g2.e_mat = ae; g2.lde = pl.lda;
                 g2.alpha = k.b; g2.beta = k.c;
-                nb_sym += g1.tiles_per_mat * pl.cnt;
+                nb_sym += g2.tiles_per_mat * pl.cnt;
                 // X' = a X + B X
                 GemmArgs& g3 = bx.seg[ci];
                 g3.first_block = nb_bx;
@@ -453,13 +486,13 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             }
             // the symmetric products' K differs between segments (X X^T: n);
             // deal whole matrices over the XCDs when the tile counts agree
-            {
-                int tpm = syrk.seg[0].tiles_per_mat;
+            for (GemmLaunch* L : {&syrk, &aab}) {
+                int tpm = L->seg[0].tiles_per_mat;
                 for (int ci = 1; ci < nseg; ++ci)
-                    if (syrk.seg[ci].tiles_per_mat != tpm) tpm = 0;
-                syrk.interleave_tpm = aab.interleave_tpm = tpm;
+                    if (L->seg[ci].tiles_per_mat != tpm) tpm = 0;
+                L->interleave_tpm = tpm;
             }
-            e = launch_gemm(GEMM_SYRK, grp.tile, grp.tile, syrk, nb_sym, nullptr, stream);
+            e = launch_gemm(GEMM_SYRK, syrk_tile, syrk_tile, syrk, nb_syrk, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
             e = launch_gemm(GEMM_AAB, grp.tile, grp.tile, aab, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");

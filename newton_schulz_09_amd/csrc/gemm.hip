@@ -154,11 +154,13 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KIND>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
-    static_assert(!SYM || (BM == BN && WGM == WGN), "symmetric products use square tiles and wave grids");
+    static_assert(!SYM || BM == BN, "symmetric products use square tiles");
     static_assert(BK == 64 || BK == 32, "BK is 32 or 64");
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
     constexpr int NW = WGM * WGN;              // wavefronts per workgroup
     constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave sub-tile
+    static_assert(!SYM || WGM == WGN || (WTN == 64 && WTM % 64 == 0),
+                  "a non-square wave grid of a symmetric product handles diagonal tiles in 64 x 64 blocks");
     constexpr int FM = WTM / 32, FN = WTN / 32;
     // a X + B X reads its second operand, X, in its own row-major layout ("NN"):
     // the Q tile is BK rows of K by BN columns, and the MFMA fragments (8
@@ -687,7 +689,83 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
         }
     };
 
-    if constexpr (SYM) {
+    if constexpr (SYM && WGM != WGN) {
+        // non-square wave grid (sub-tiles of WTM x 64): off-diagonal tiles as
+        // below; on a diagonal tile each 64 x 64 block of the wave's sub-tile
+        // lies wholly above the diagonal (stored with its mirror), on it
+        // (symmetrised, stored once) or wholly below (the mirror of another)
+        bf16_t* C = args.C + cm * args.c_mat;
+        if (ti != tj) {
+            put_t();
+            lds_fence();
+            store_bf16(std::integral_constant<int, CT_>{}, WTN, 0, C + static_cast<int64_t>(j0w) * args.ldc + i0w,
+                       args.ldc);
+            lds_fence();
+            put_n(false);
+            lds_fence();
+            store_bf16(std::integral_constant<int, CN_>{}, WTM, 2, C + static_cast<int64_t>(i0w) * args.ldc + j0w,
+                       args.ldc);
+        } else {
+#pragma unroll
+            for (int b = 0; b < WTM / 64; ++b) {
+                const int rb = wm * WTM + 64 * b, cb = wn * 64;  // tile-local origin of the block
+                if (rb > cb) continue;
+                const int gi = i0 + rb, gj = j0 + cb;
+                // the block's two fragment rows, staged as a 64 x 64 tile
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int fm = 2 * b + f;
+                            const int jj = fn * 32 + (lane & 31);
+                            const int ib = f * 32 + 8 * g4 + 4 * (lane >> 5);
+                            const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
+                            if (rb < cb) {  // above: the mirror [jj][ii] first (8-byte pieces)
+                                *reinterpret_cast<u32x2*>(W + jj * 64 + (eslot<8>(ib >> 3, jj) << 3) + (ib & 7)) =
+                                    hv[fm][fn][g4];
+                            } else {  // on the diagonal: keep ii <= jj and mirror it
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const int ii = ib + q;
+                                    if (ii <= jj) {
+                                        const bf16_t h = static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+                                        W[ii * 64 + (eslot<8>(jj >> 3, ii >> 2) << 3) + (jj & 7)] = h;
+                                        W[jj * 64 + (eslot<8>(ii >> 3, jj >> 2) << 3) + (ii & 7)] = h;
+                                    }
+                                }
+                            }
+                        }
+                lds_fence();
+                if (rb < cb) {
+                    store_bf16(std::integral_constant<int, 8>{}, 64, 0, C + static_cast<int64_t>(gj) * args.ldc + gi,
+                               args.ldc);
+                    lds_fence();
+                    // then the block itself [ii][jj] (2-byte pieces)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                const int fm = 2 * b + f;
+                                const int jj = fn * 32 + (lane & 31);
+                                const int ib = f * 32 + 8 * g4 + 4 * (lane >> 5);
+                                const uint32_t w2[2] = {hv[fm][fn][g4].x, hv[fm][fn][g4].y};
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    W[(ib + q) * 64 + (eslot<8>(jj >> 3, ib >> 2) << 3) + (jj & 7)] =
+                                        static_cast<bf16_t>((w2[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+                            }
+                    lds_fence();
+                }
+                store_bf16(std::integral_constant<int, 8>{}, 64, 2, C + static_cast<int64_t>(gi) * args.ldc + gj,
+                           args.ldc);
+                lds_fence();
+            }
+        }
+    } else if constexpr (SYM) {
         bf16_t* C = args.C + cm * args.c_mat;
         if (ti != tj || wm < wn) {
             // off-diagonal block: the block itself and its mirror
@@ -772,7 +850,7 @@ hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTab
     constexpr int NT = 64 * WGM * WGN;
     PtrTable o{};
     if (out) o = *out;
-    if constexpr (BM == BN && WGM == WGN) {
+    if constexpr (BM == BN) {
         switch (kind) {
             case GEMM_SYRK:
                 k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_SYRK><<<grid, NT, 0, stream>>>(L, o);
@@ -817,6 +895,14 @@ hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& la
         return (s && atoi(s) == 4) ? 4 : 8;
     }();
     if (tile == 256 && bx_waves == 8 && (kind == GEMM_BX || kind == GEMM_BX_FINAL))
+        return launch_t<256, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
+    // 256 x 256 tiles of X X^T: 8 waves (2 x 4, each 128 x 64; diagonal tiles
+    // in 64 x 64 blocks); MUON_SYRK_WAVES=4 selects the 4-wave engine
+    static const int syrk_waves = [] {
+        const char* s = getenv("MUON_SYRK_WAVES");
+        return (s && atoi(s) == 4) ? 4 : 8;
+    }();
+    if (tile == 256 && syrk_waves == 8 && kind == GEMM_SYRK)
         return launch_t<256, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
     // K pipeline: 0 = BK 64 with 2 stages, 1 = BK 32 with 4 stages,
     // 2 = BK 32 with 2 stages for tiles up to 128 (half the LDS, so more

@@ -106,8 +106,10 @@ def test_single_64x128_after_momentum_and_transpose(muon):
     assert parity.is_bf16_valued(o)
 
 
+# (1000, 1600), (500, 1024) and (1024, 500) pad m to a multiple of 256, so
+# X X^T runs on 256 x 256 tiles with padding inside its diagonal tiles
 SHAPES = [(1, 1), (1, 9), (9, 1), (3, 5), (5, 3), (64, 64), (65, 130), (130, 65), (100, 1000),
-          (257, 300), (640, 700), (700, 640), (768, 768), (1000, 1600), (96, 4000)]
+          (257, 300), (640, 700), (700, 640), (768, 768), (1000, 1600), (96, 4000), (500, 1024), (1024, 500)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
