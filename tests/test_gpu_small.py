@@ -214,6 +214,26 @@ def test_batched_many_shapes_and_passes(muon):
     _bitwise_equal_to_single(muon, Gs[100:104], outs[100:104])
 
 
+@pytest.mark.parametrize("shapes", [
+    # 120 x 3 + 8 x 3 = 384 tiles of 256 x 256 in one a X + B X launch: more
+    # than one round on 256 CUs, a partial last round that holds every tall
+    # matrix (the final step writes those transposed)
+    [(256, 768)] * 120 + [(768, 256)] * 8,
+    # 8 x 36 = 288 tiles
+    [(768, 3072)] * 8,
+])
+def test_batched_large_launches_equal_single_calls(muon, shapes):
+    """Launches of several rounds of 256 x 256 tiles give every matrix exactly
+    what a single call (a few tiles) gives it, and match the oracle."""
+    rng = np.random.default_rng(31)
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = muon.ns5_batched(Gs)
+    _bitwise_equal_to_single(muon, Gs, outs)
+    for k in sorted({len(shapes) * 7 // 8, len(shapes) - 1}):  # tiles of the last round
+        parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(host[k]), f"{shapes[k]} #{k}")
+
+
 def test_batched_zero_steps_and_aliasing(muon):
     rng = np.random.default_rng(11)
     host = [rng.standard_normal(s).astype(np.float32) for s in [(70, 90), (90, 70), (33, 33)]]
