@@ -65,6 +65,13 @@ def round_bf16(x):
     return r
 
 
+def round_f32(x):
+    """Round float64 values to the nearest float32 value, ties to even (the
+    IEEE conversion), returned as float64 holding float32-representable
+    values."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def momentum_nesterov(g, buf, mu=0.95):
     """One Nesterov-momentum step on a gradient, as the Muon section uses it
     (summary paragraph: "Nesterov momentum in the update, orthogonalise after
@@ -85,7 +92,7 @@ def momentum_nesterov(g, buf, mu=0.95):
     return buf_new, u
 
 
-def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):
+def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS, precision="bf16"):
     """Quintic Newton-Schulz orthogonalisation of one 2-D matrix, following the
     Muon section's ``zeroth_power_via_newtonschulz5`` step by step:
 
@@ -100,7 +107,16 @@ def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):
 
     The Frobenius norm is taken of the float32 input in float64 and is never
     rounded to bf16.  Returns a float32 array of G's shape.
+
+    ``precision="f32"``: the same iteration carried in float32 instead of
+    bfloat16, the precision the summary paragraph contrasts with bf16 (it
+    notes the iteration stays stable in bf16, unlike methods that need
+    float32): there is no bf16 cast, X = G / (||G||_F + eps) is rounded once
+    to float32, and A, B and X of every step are rounded once to float32 at
+    the same points.
     """
+    if precision not in ("bf16", "f32"):
+        raise ValueError("precision is 'bf16' or 'f32'")
     G = np.asarray(G)
     if G.ndim != 2:
         raise ValueError("ns5 expects a 2-D matrix")
@@ -108,14 +124,19 @@ def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):
     eps = f32(eps)
     u = G.astype(np.float32).astype(np.float64)
     norm = np.sqrt(np.sum(u * u))
-    X = round_bf16(round_bf16(u) / (norm + eps))
+    if precision == "bf16":
+        rnd = round_bf16
+        X = rnd(rnd(u) / (norm + eps))
+    else:
+        rnd = round_f32
+        X = rnd(u / (norm + eps))
     tall = G.shape[0] > G.shape[1]
     if tall:
         X = X.T
     for _ in range(steps):
-        A = round_bf16(X @ X.T)
-        B = round_bf16(b * A + c * (A @ A))
-        X = round_bf16(a * X + B @ X)
+        A = rnd(X @ X.T)
+        B = rnd(b * A + c * (A @ A))
+        X = rnd(a * X + B @ X)
     if tall:
         X = X.T
     return np.ascontiguousarray(X).astype(np.float32)
