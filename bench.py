@@ -21,6 +21,9 @@ Printed (one JSON line on stdout):
   ns5_4096       NS5 of one 4096x4096 matrix (U diag(s) V^T, seed 3)
   apply_step     the same step with the parameter update p <- p - lr * O
                  fused into the last epilogue (muon_momentum_ns5_apply_batched)
+  f32_iteration  the same 48 matrices through the iteration carried in float32
+                 (muon_newton_schulz_f32_batched), against the float32 matrix
+                 peak, and its time over the bf16 NS5 of the same matrices
   cpu_baseline   the CPU oracle on a bounded sample of the same step
 """
 
@@ -37,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "NS5 TFLOP/s (bf16) & % MFMA peak; ms per GPT-2-124M-shaped Muon step"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense float32 matrix-core peak (published)
 
 
 def log(*a):
@@ -203,6 +207,31 @@ def time_square(torch, muon, workloads, reps=10):
     return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def time_f32_iteration(st, torch, muon, reps=3):
+    """The same 48 matrices through the iteration carried in float32
+    (muon_newton_schulz_f32_batched: no bf16 anywhere, float32 MFMA products),
+    next to NS5 of the same matrices in bf16 (muon_ns5_batched), both on the
+    momentum outputs already in HBM."""
+    st.momentum()   # u = g + mu buf: real values (constant operands would flatter the matrix cores)
+    outs = [torch.empty_like(u) for u in st.us]
+    ws = torch.empty(muon.f32_workspace_size(st.shapes), dtype=torch.uint8, device=st.device)
+    timings = {}
+    for name, fn in (("f32", lambda: muon.newton_schulz_f32(st.us, outs, workspace=ws)),
+                     ("bf16", lambda: muon.ns5_batched(st.us, outs, workspace=st.workspace))):
+        fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        timings[name] = start.elapsed_time(stop) / reps
+    tf = st.nominal_ns5_flops() / (timings["f32"] * 1e-3) / 1e12
+    return {"ms": round(timings["f32"], 3), "TFLOP/s": round(tf, 2), "pct_f32_mfma_peak": round(100 * tf / PEAK_F32_TFLOPS, 2),
+            "bf16_ns5_ms": round(timings["bf16"], 4), "f32_over_bf16": round(timings["f32"] / timings["bf16"], 2)}
+
+
 def cpu_baseline(items):
     """The oracle, as it stands, on the whole step (all 48 matrices: momentum
     then NS5), timed on this host's cores."""
@@ -287,6 +316,8 @@ def main():
         log(f"momentum: {res['momentum']}")
         res["apply_step"] = time_apply_step(st, args.steps, torch)
         log(f"apply step: {res['apply_step']}")
+        res["f32_iteration"] = time_f32_iteration(st, torch, muon)
+        log(f"float32 iteration: {res['f32_iteration']}")
         if not args.skip_square:
             res["ns5_4096"] = time_square(torch, muon, workloads)
             log(f"ns5 4096: {res['ns5_4096']}")

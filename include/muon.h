@@ -175,6 +175,41 @@ int muon_newton_schulz_batched(const float* const* G, float* const* out, const i
                                size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes for muon_newton_schulz_f32_batched on these shapes (0 if a
+ * shape is invalid or beyond MUON_NS5_MAX_SHORT / MUON_NS5_MAX_LONG).
+ */
+size_t muon_newton_schulz_f32_workspace_size(const int64_t* rows, const int64_t* cols, int64_t count);
+
+/*
+ * The iteration carried in float32 instead of bfloat16: the contrast the
+ * summary paragraph of the Muon section (Synced report on Modded-NanoGPT)
+ * draws when it notes that the Newton-Schulz iteration stays stable in bf16,
+ * unlike methods that need float32.  The steps of the printed
+ * zeroth_power_via_newtonschulz5 with float32 in place of bf16: no bf16 cast
+ * of the input, X0 = G / (||G||_F + eps) rounded once to float32 (the quotient
+ * formed in float64), transposed when rows > cols; then `steps` times
+ * A = X X^T, B = b A + c A A, X = a X + B X, each stored matrix rounded once
+ * to float32 (float32 MFMA products with float32 accumulation); the result in
+ * G's orientation.  For comparison with the bf16 path: about 16 times the
+ * MFMA time per flop (float32 dense peak 157.3 TFLOP/s against 2.5 PFLOP/s).
+ *  G, out, rows, cols, count, steps, eps : as muon_ns5_batched (float32,
+ *          device pointers, host arrays; out may alias G).
+ *  coeffs : host array of 3 finite floats (a, b, c), or NULL for NS5's
+ *          (MUON_NS5_A, MUON_NS5_B, MUON_NS5_C).
+ *  workspace : device memory of at least
+ *          muon_newton_schulz_f32_workspace_size(rows, cols, count) bytes,
+ *          256-byte aligned, owned by the caller; contents on entry are
+ *          ignored and on return undefined.  Same-shaped matrices run in
+ *          passes of up to MUON_NS5_MAX_GROUP, one launch per product and
+ *          step; shapes run one after another.
+ * Errors: as muon_ns5_batched, plus MUON_ERR_INVALID_ARG for a non-finite
+ * coefficient.
+ */
+int muon_newton_schulz_f32_batched(const float* const* G, float* const* out, const int64_t* rows,
+                                   const int64_t* cols, int64_t count, int steps, const float* coeffs, float eps,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * NS5 of bfloat16 matrices, returning bfloat16 (as muon_ns5_batched, whose
  * inputs and outputs are float32).  The printed listing of the Muon section
  * (Synced report on Modded-NanoGPT) casts G to bfloat16 before the iteration

@@ -608,6 +608,184 @@ int run_batched(const float* const* G, float* const* out, float* const* buf, flo
     return run_groups(groups, k, up, mu, steps, eps, static_cast<char*>(ws), stream, sink);
 }
 
+// ---- the iteration carried in float32 (f32_iter.hip)
+//
+// Per pass of up to kMaxGroup same-shaped matrices the workspace holds float32
+// X[2] (mp x ldx), A and B (mp x lda) and the float64 norm partials; m and n
+// are padded to the 128 tile, rows carry a 32-float skew.  Passes run one
+// after another, each reusing the workspace from its start.
+constexpr int kF32Tile = 128;
+
+struct F32Plan {
+    int64_t rows, cols;
+    int m, n, mp, np, ldx, lda, nb, cnt;
+    bool tall;
+    size_t off_x[2], off_a, off_b, off_part, bytes;
+};
+
+bool plan_f32(int64_t rows, int64_t cols, int64_t count, F32Plan* p) {
+    if (rows < 1 || cols < 1 || count < 1) return false;
+    const int64_t m = rows < cols ? rows : cols;
+    const int64_t n = rows < cols ? cols : rows;
+    if (m > MUON_NS5_MAX_SHORT || n > MUON_NS5_MAX_LONG) return false;
+    p->rows = rows;
+    p->cols = cols;
+    p->m = static_cast<int>(m);
+    p->n = static_cast<int>(n);
+    p->tall = rows > cols;
+    p->mp = static_cast<int>(round_up(m, kF32Tile));
+    p->np = static_cast<int>(round_up(n, kF32Tile));
+    p->ldx = p->np + 32;
+    p->lda = p->mp + 32;
+    int64_t nb = (rows * cols + 16383) / 16384;
+    p->nb = static_cast<int>(nb < 1 ? 1 : (nb > kMaxNormBlocks ? kMaxNormBlocks : nb));
+    const int64_t tiles = static_cast<int64_t>(p->mp / kF32Tile) * (p->np / kF32Tile);
+    int64_t cnt = count < kMaxGroup ? count : kMaxGroup;
+    if (cnt * tiles > kMaxWorkgroups) cnt = kMaxWorkgroups / tiles;
+    if (cnt < 1) return false;
+    p->cnt = static_cast<int>(cnt);
+    const size_t xb = align256(static_cast<size_t>(cnt) * p->mp * p->ldx * sizeof(float));
+    const size_t ab = align256(static_cast<size_t>(cnt) * p->mp * p->lda * sizeof(float));
+    size_t off = 0;
+    p->off_x[0] = off; off += xb;
+    p->off_x[1] = off; off += xb;
+    p->off_a = off; off += ab;
+    p->off_b = off; off += ab;
+    p->off_part = off; off += align256(static_cast<size_t>(cnt) * p->nb * sizeof(double));
+    p->bytes = off;
+    return true;
+}
+
+// Workspace bytes of a validated batch: the largest pass.
+int f32_bytes(const std::vector<Segment>& segs, size_t* bytes) {
+    *bytes = 0;
+    for (const Segment& sg : segs) {
+        F32Plan pl;
+        if (!plan_f32(sg.rows, sg.cols, sg.count, &pl))
+            return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits", (long long)sg.rows,
+                        (long long)sg.cols);
+        if (pl.bytes > *bytes) *bytes = pl.bytes;
+    }
+    return MUON_OK;
+}
+
+int run_f32(const float* const* G, float* const* out, const int64_t* rows, const int64_t* cols, int64_t count,
+            int steps, const Coeffs& k, float eps, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_common(steps, eps);
+    if (st) return st;
+    std::vector<Segment> segs;
+    std::vector<std::vector<const float*>> gs;
+    std::vector<std::vector<float*>> os, bs;
+    st = batched_segments(G, out, nullptr, rows, cols, count, true, &segs, &gs, &os, &bs);
+    if (st) return st;
+    size_t need = 0;
+    st = f32_bytes(segs, &need);
+    if (st) return st;
+    st = check_workspace(ws, ws_bytes, need);
+    if (st) return st;
+    (void)hipGetLastError();  // start from a clean error state
+    char* base = static_cast<char*>(ws);
+    for (const Segment& sg : segs) {
+        for (int64_t start = 0; start < sg.count;) {
+            F32Plan pl;
+            plan_f32(sg.rows, sg.cols, sg.count - start, &pl);
+            const int cnt = pl.cnt;
+            ConstPtrTable gt{};
+            PtrTable ot{};
+            bool vec = (pl.rows * pl.cols) % 4 == 0;
+            for (int i = 0; i < cnt; ++i) {
+                gt.p[i] = sg.G[start + i];
+                ot.p[i] = sg.out[start + i];
+                vec = vec && (reinterpret_cast<uintptr_t>(gt.p[i]) & 15u) == 0;
+            }
+            float* X[2] = {reinterpret_cast<float*>(base + pl.off_x[0]), reinterpret_cast<float*>(base + pl.off_x[1])};
+            float* A = reinterpret_cast<float*>(base + pl.off_a);
+            float* B = reinterpret_cast<float*>(base + pl.off_b);
+            double* part = reinterpret_cast<double*>(base + pl.off_part);
+            // the norm's float64 partial sums (the pass the bf16 iteration uses)
+            NormLaunch nl{};
+            nl.nseg = 1;
+            NormSeg& ns = nl.seg[0];
+            ns.first_block = 0;
+            ns.nb = pl.nb;
+            ns.ptr_base = 0;
+            ns.vec = vec ? 1 : 0;
+            ns.numel = pl.rows * pl.cols;
+            ns.chunk = (ns.numel + pl.nb - 1) / pl.nb;
+            if (vec) ns.chunk = (ns.chunk + 3) / 4 * 4;
+            ns.ub = nullptr;
+            ns.ub_mat = 0;
+            ns.partials = part;
+            hipError_t e = launch_norm(nl, pl.nb * cnt, gt, nullptr, 0.0f, stream);
+            if (e != hipSuccess) return hip_fail(e, "norm (sum of squares) launch");
+            F32Scale sc{};
+            sc.partials = part;
+            sc.nb = pl.nb;
+            sc.rows = static_cast<int>(pl.rows);
+            sc.cols = static_cast<int>(pl.cols);
+            sc.tall = pl.tall ? 1 : 0;
+            sc.eps = eps;
+            if (steps == 0) {  // X0 itself, in G's orientation
+                sc.to_out = 1;
+                sc.tiles_c = static_cast<int>((pl.cols + 31) / 32);
+                sc.tiles_per_mat = static_cast<int>((pl.rows + 31) / 32) * sc.tiles_c;
+                e = launch_f32_scale(sc, sc.tiles_per_mat * cnt, gt, &ot, stream);
+                if (e != hipSuccess) return hip_fail(e, "float32 scale launch");
+                start += cnt;
+                continue;
+            }
+            sc.to_out = 0;
+            sc.X = X[0];
+            sc.x_mat = static_cast<int64_t>(pl.mp) * pl.ldx;
+            sc.ldx = pl.ldx;
+            sc.tiles_c = pl.np / 32;
+            sc.tiles_per_mat = (pl.mp / 32) * sc.tiles_c;
+            e = launch_f32_scale(sc, sc.tiles_per_mat * cnt, gt, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "float32 scale launch");
+            const int tm = pl.mp / kF32Tile, tn = pl.np / kF32Tile;
+            const int64_t xe = static_cast<int64_t>(pl.mp) * pl.ldx, ae = static_cast<int64_t>(pl.mp) * pl.lda;
+            int cur = 0;
+            for (int s = 0; s < steps; ++s) {
+                const int nxt = cur ^ 1;
+                const bool last = s == steps - 1;
+                F32Gemm g1{};  // A = X X^T
+                g1.P = X[cur]; g1.p_mat = xe; g1.ldp = pl.ldx;
+                g1.Q = X[cur]; g1.q_mat = xe; g1.ldq = pl.ldx;
+                g1.C = A; g1.c_mat = ae; g1.ldc = pl.lda;
+                g1.K = pl.np;
+                g1.tiles = tm; g1.tiles_n = tm; g1.tiles_per_mat = tm * (tm + 1) / 2;
+                e = launch_f32_gemm(GEMM_SYRK, g1, g1.tiles_per_mat * cnt, nullptr, stream);
+                if (e != hipSuccess) return hip_fail(e, "float32 X X^T launch");
+                F32Gemm g2{};  // B = b A + c A A
+                g2.P = A; g2.p_mat = ae; g2.ldp = pl.lda;
+                g2.Q = A; g2.q_mat = ae; g2.ldq = pl.lda;
+                g2.C = B; g2.c_mat = ae; g2.ldc = pl.lda;
+                g2.E = A; g2.e_mat = ae; g2.lde = pl.lda;
+                g2.alpha = k.b; g2.beta = k.c;
+                g2.K = pl.mp;
+                g2.tiles = tm; g2.tiles_n = tm; g2.tiles_per_mat = tm * (tm + 1) / 2;
+                e = launch_f32_gemm(GEMM_AAB, g2, g2.tiles_per_mat * cnt, nullptr, stream);
+                if (e != hipSuccess) return hip_fail(e, "float32 b A + c A A launch");
+                F32Gemm g3{};  // X' = a X + B X
+                g3.P = B; g3.p_mat = ae; g3.ldp = pl.lda;
+                g3.Q = X[cur]; g3.q_mat = xe; g3.ldq = pl.ldx;
+                g3.C = X[nxt]; g3.c_mat = xe; g3.ldc = pl.ldx;
+                g3.E = X[cur]; g3.e_mat = xe; g3.lde = pl.ldx;
+                g3.alpha = k.a;
+                g3.K = pl.mp;
+                g3.tiles = tm; g3.tiles_n = tn; g3.tiles_per_mat = tm * tn;
+                g3.m = pl.m; g3.n = pl.n; g3.tall = pl.tall ? 1 : 0;
+                e = launch_f32_gemm(last ? GEMM_BX_FINAL : GEMM_BX, g3, g3.tiles_per_mat * cnt, last ? &ot : nullptr,
+                                    stream);
+                if (e != hipSuccess) return hip_fail(e, "float32 a X + B X launch");
+                cur = nxt;
+            }
+            start += cnt;
+        }
+    }
+    return ok();
+}
+
 }  // namespace
 
 }  // namespace muon
@@ -728,6 +906,33 @@ int muon_momentum_ns5_apply_batched(const float* const* g, float* const* buf, fl
     up.lr = lr;
     return run_batched(g, p, buf, mu, rows, cols, count, steps, eps, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream), nullptr, kQuintic, up);
+}
+
+size_t muon_newton_schulz_f32_workspace_size(const int64_t* rows, const int64_t* cols, int64_t count) {
+    using namespace muon;
+    const std::string saved = g_last_error;
+    std::vector<Segment> segs;
+    std::vector<std::vector<const float*>> gs;
+    std::vector<std::vector<float*>> os, bs;
+    size_t bytes = 0;
+    int st = batched_segments(nullptr, nullptr, nullptr, rows, cols, count, false, &segs, &gs, &os, &bs);
+    if (!st) st = f32_bytes(segs, &bytes);
+    g_last_error = saved;
+    return st ? 0 : bytes;
+}
+
+int muon_newton_schulz_f32_batched(const float* const* G, float* const* out, const int64_t* rows,
+                                   const int64_t* cols, int64_t count, int steps, const float* coeffs, float eps,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    Coeffs k = kQuintic;
+    if (coeffs) {
+        for (int i = 0; i < 3; ++i)
+            if (!isfinite(coeffs[i])) return fail(MUON_ERR_INVALID_ARG, "coefficient %d is not finite", i);
+        k = Coeffs{coeffs[0], coeffs[1], coeffs[2]};
+    }
+    return run_f32(G, out, rows, cols, count, steps, k, eps, workspace, workspace_bytes,
+                   static_cast<hipStream_t>(stream));
 }
 
 int muon_ns5_batched_timed(const float* const* G, float* const* out, float* const* buf, float mu,

@@ -155,4 +155,46 @@ hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const 
 hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& launch, int blocks,
                        const PtrTable* out, hipStream_t stream);
 
+// The iteration carried in float32 (f32_iter.hip): one launch per product
+// over `cnt` same-shaped matrices, 128 x 128 output tiles, float32 operands
+// padded to whole tiles (the padding stays zero, as in the bf16 iteration).
+// C = P Q with P M x K row-major; Q N x K row-major (X X^T) or K x N
+// row-major (A A, B X); E is the fused update's second operand.
+struct F32Gemm {
+    const float* P;
+    int64_t p_mat;
+    int ldp;
+    const float* Q;
+    int64_t q_mat;
+    int ldq;
+    float* C;
+    int64_t c_mat;
+    int ldc;
+    const float* E;
+    int64_t e_mat;
+    int lde;
+    float alpha, beta;  // b A + c A A: alpha = b, beta = c; a X + B X: alpha = a
+    int K;              // a multiple of 16
+    int tiles, tiles_n, tiles_per_mat;
+    int m, n, tall;     // last step: the output is m x n (or its transpose when tall)
+};
+hipError_t launch_f32_gemm(GemmKind kind, const F32Gemm& g, int blocks, const PtrTable* out, hipStream_t stream);
+
+// X0 = G / (||G|| + eps) in float32 from the float64 norm partials (nb per
+// matrix), into X (padded, transposed when G is tall) or (to_out) into the
+// outputs in G's orientation.  32 x 32 tiles: tiles_c per row of tiles.
+struct F32Scale {
+    const double* partials;
+    int nb;
+    int rows, cols, tall;
+    float* X;
+    int64_t x_mat;
+    int ldx;
+    int tiles_c, tiles_per_mat;
+    int to_out;
+    float eps;
+};
+hipError_t launch_f32_scale(const F32Scale& s, int blocks, const ConstPtrTable& G, const PtrTable* out,
+                            hipStream_t stream);
+
 }  // namespace muon

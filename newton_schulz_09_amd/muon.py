@@ -32,7 +32,7 @@ MAX_GROUP = 128
 EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
            "muon_ns5_batched_bf16", "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
-           "muon_ns5_batched_timed",
+           "muon_ns5_batched_timed", "muon_newton_schulz_f32_workspace_size", "muon_newton_schulz_f32_batched",
            "muon_status_string", "muon_last_error")
 
 
@@ -80,6 +80,12 @@ def _load():
                                            ctypes.c_float, pi64, pi64, i64, ctypes.c_int, ctypes.c_float, vp, sz,
                                            vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.muon_ns5_batched_timed.restype = ctypes.c_int
+    lib.muon_newton_schulz_f32_workspace_size.argtypes = [pi64, pi64, i64]
+    lib.muon_newton_schulz_f32_workspace_size.restype = sz
+    lib.muon_newton_schulz_f32_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), pi64, pi64, i64,
+                                                   ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
+                                                   vp, sz, vp]
+    lib.muon_newton_schulz_f32_batched.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
@@ -313,6 +319,52 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
                                           float(eps), ws.data_ptr(), nbytes, stream, ev, len(events) // 2,
                                           ctypes.byref(rec)))
         ns5_batched.last_recorded = rec.value
+    return outs
+
+
+def f32_workspace_size(shapes):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * n)(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * n)(*[int(s[1]) for s in shapes])
+    return int(lib.muon_newton_schulz_f32_workspace_size(rows, cols, n))
+
+
+def newton_schulz_f32(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, coeffs=None, workspace=None):
+    """The iteration carried in float32 (muon_newton_schulz_f32_batched): for
+    each float32 matrix of ``Gs`` (any shapes, one device), X0 = G / (||G|| +
+    eps) in float32 and ``steps`` steps X <- a X + (b A + c A A) X with every
+    stored matrix in float32; ``coeffs`` (a, b, c) defaults to NS5's.  Returns
+    the list of outputs (new tensors unless given)."""
+    Gs = list(Gs)
+    if not Gs:
+        return []
+    for i, G in enumerate(Gs):
+        _require_f32_cuda(G, f"Gs[{i}]")
+        if G.dim() != 2:
+            raise ValueError(f"Gs[{i}] must be 2-D")
+    device = Gs[0].device
+    if any(G.device != device for G in Gs):
+        raise ValueError("all matrices must be on one device")
+    outs = _outputs(Gs, outs)
+    count = len(Gs)
+    shapes = [tuple(G.shape) for G in Gs]
+    need = f32_workspace_size(shapes)
+    if need == 0:
+        raise MuonError(MUON_ERR_UNSUPPORTED, "a shape is not supported")
+    stream = _stream_handle(device)
+    ws = workspace if workspace is not None else _workspace(device, stream, need)
+    rows = (ctypes.c_int64 * count)(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * count)(*[s[1] for s in shapes])
+    g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
+    o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    k = None
+    if coeffs is not None:
+        k = tuple(float(c) for c in coeffs)
+        if len(k) != 3:
+            raise ValueError("coeffs must be (a, b, c)")
+        k = (ctypes.c_float * 3)(*k)
+    _check(lib.muon_newton_schulz_f32_batched(g_ptrs, o_ptrs, rows, cols, count, int(steps), k, float(eps),
+                                              ws.data_ptr(), ws.numel() * ws.element_size(), stream))
     return outs
 
 

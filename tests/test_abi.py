@@ -222,3 +222,46 @@ def test_bf16_validation_errors_before_any_launch(muon):
     assert call(g, o, rows, cols, 2, -1, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
     assert call(g, o, rows, cols, 2, 5, float("nan"), ws, need, None) == muon.MUON_ERR_INVALID_ARG
     assert call(g, o, rows, cols, 2, 5, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+
+
+def test_f32_workspace_size(muon):
+    # X twice + A, B in float32, padded to the 128 tile with a 32-float row skew
+    s = muon.f32_workspace_size([(64, 128)])
+    assert s >= 2 * 128 * 160 * 4 + 2 * 128 * 160 * 4
+    assert muon.f32_workspace_size([(128, 64)]) == s            # orientation-independent
+    one = muon.f32_workspace_size([(768, 2304)])
+    assert muon.f32_workspace_size([(768, 2304)] * 12) > 11 * one
+    # shapes run one after another: the largest pass sets the size
+    assert muon.f32_workspace_size([(768, 2304)] * 12 + [(64, 128)]) == muon.f32_workspace_size([(768, 2304)] * 12)
+    assert muon.f32_workspace_size([(768, 2304)] * 500) == muon.f32_workspace_size([(768, 2304)] * 128)
+    assert muon.f32_workspace_size([(0, 5)]) == 0
+    assert muon.f32_workspace_size([(20000, 20000)]) == 0
+
+
+def test_f32_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    need = lib.muon_newton_schulz_f32_workspace_size(rows, cols, 2)
+    assert need > 0
+    call = lib.muon_newton_schulz_f32_batched
+    ok = (ctypes.c_float * 3)(1.5, -0.5, 0.0)
+    nan = (ctypes.c_float * 3)(1.5, float("inf"), 0.0)
+    assert call(g, o, rows, cols, 2, 5, nan, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"coefficient 1" in lib.muon_last_error()
+    assert call(g, o, rows, cols, 2, 5, ok, 1e-7, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+    assert call(g, o, rows, cols, 2, 5, None, 1e-7, ctypes.c_void_p(0x200010), need, None) == muon.MUON_ERR_WORKSPACE
+    assert call(g, o, rows, cols, 2, 5, None, 1e-7, None, need, None) == muon.MUON_ERR_WORKSPACE
+    assert call(g, o, rows, cols, 2, -1, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, cols, 2, 5, None, float("nan"), ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(None, o, rows, cols, 2, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, rows, cols, 0, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    bad = (i64 * 2)(64, 0)
+    assert call(g, o, bad, cols, 2, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    null_o = (ctypes.c_void_p * 2)(0x300000, None)
+    assert call(g, null_o, rows, cols, 2, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    big = (i64 * 1)(20000)
+    assert call(g, o, big, big, 1, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_UNSUPPORTED
