@@ -97,11 +97,10 @@ __global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G
     const int64_t end = begin + sg.chunk < sg.numel ? begin + sg.chunk : sg.numel;
     double s0 = 0.0, s1 = 0.0;
     if (sg.vec) {
-        for (int64_t i = begin + 4 * static_cast<int64_t>(threadIdx.x); i < end; i += 4 * kThreads) {
-            const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
+        // four consecutive elements at i: momentum, staging, sum of squares
+        auto step4 = [&](int64_t i, const f32x4& gv, f32x4 bv) {
             float u[4];
             if constexpr (MOM) {
-                f32x4 bv = *reinterpret_cast<const f32x4*>(buf + i);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     bv[q] = fmaf(mu, bv[q], gv[q]);
@@ -119,6 +118,21 @@ __global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G
             s1 = fma(static_cast<double>(u[1]), static_cast<double>(u[1]), s1);
             s0 = fma(static_cast<double>(u[2]), static_cast<double>(u[2]), s0);
             s1 = fma(static_cast<double>(u[3]), static_cast<double>(u[3]), s1);
+        };
+        // two groups per iteration (all their loads in flight together), in
+        // the same per-thread order as one group at a time
+        for (int64_t i = begin + 4 * static_cast<int64_t>(threadIdx.x); i < end; i += 8 * kThreads) {
+            const int64_t i2 = i + 4 * kThreads;
+            const bool two = i2 < end;
+            const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
+            f32x4 bv{}, gv2{}, bv2{};
+            if constexpr (MOM) bv = *reinterpret_cast<const f32x4*>(buf + i);
+            if (two) {
+                gv2 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i2));
+                if constexpr (MOM) bv2 = *reinterpret_cast<const f32x4*>(buf + i2);
+            }
+            step4(i, gv, bv);
+            if (two) step4(i2, gv2, bv2);
         }
     } else {
         for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
@@ -227,6 +241,11 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     __shared__ double s_norm;
     __shared__ __attribute__((aligned(16))) bf16_t tile_t[kCastTile][kCastTile + 8];  // [col][row]
 
+    // the first tile's loads go out before the norm reduction, which they do
+    // not depend on
+    float v[2][8], vn[2][8];
+    cast_load<BF16IN>(g, u16, rows, cols, vec, (t_begin / sg.tiles_c) * kCastTile,
+                      (t_begin % sg.tiles_c) * kCastTile, v);
     if (wave == 0) {
         const double* part = sg.partials + static_cast<int64_t>(mat) * sg.nb;
         double s = 0.0;
@@ -244,9 +263,6 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     const float r32 = static_cast<float>(1.0 / d);
     const bool fast_ok = r32 >= 0x1p-126f && r32 <= 0x1.fffffep127f;
 
-    float v[2][8], vn[2][8];
-    cast_load<BF16IN>(g, u16, rows, cols, vec, (t_begin / sg.tiles_c) * kCastTile,
-                      (t_begin % sg.tiles_c) * kCastTile, v);
     for (int t = t_begin; t < t_end; ++t) {
         const int r0 = (t / sg.tiles_c) * kCastTile, c0 = (t % sg.tiles_c) * kCastTile;
         if (t + 1 < t_end)
