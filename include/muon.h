@@ -54,6 +54,8 @@ typedef enum muon_status {
 /* Largest number of matrices one launch covers; larger groups and batches
  * are processed in passes of at most this many, reusing the workspace. */
 #define MUON_NS5_MAX_GROUP 128
+/* Matrices per launch of muon_momentum_nesterov_grouped. */
+#define MUON_NESTEROV_MAX_GROUP 64
 /* Largest supported min(rows, cols) and max(rows, cols). */
 #define MUON_NS5_MAX_SHORT 16384
 #define MUON_NS5_MAX_LONG (1 << 20)
@@ -75,6 +77,23 @@ typedef enum muon_status {
  */
 int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, float mu,
                            void* stream);
+
+/*
+ * Nesterov momentum over a list of matrices (or any float32 arrays) in one
+ * launch per MUON_NESTEROV_MAX_GROUP of them: for each i, the update of
+ * muon_momentum_nesterov on g[i], buf[i], u[i] with numel[i] elements.
+ *  g, buf, u : host arrays of `count` device pointers (float32); u[i] may
+ *          alias g[i], must not alias buf[i]; distinct i must not overlap.
+ *  numel  : host array of `count` element counts, each >= 0 (0: skipped,
+ *          its pointers may be null).
+ *  count  : >= 0; 0 enqueues nothing and returns MUON_OK.
+ * Asynchronous on `stream`; the caller owns every buffer.
+ * Errors: MUON_ERR_INVALID_ARG for count < 0, a null array, a negative
+ * numel[i], a null pointer of a non-empty entry, or u[i] == buf[i]; nothing
+ * is enqueued then.
+ */
+int muon_momentum_nesterov_grouped(const float* const* g, float* const* buf, float* const* u, const int64_t* numel,
+                                   int64_t count, float mu, void* stream);
 
 /*
  * Bytes of workspace muon_ns5 / muon_ns5_grouped need for `count` matrices of

@@ -804,6 +804,47 @@ int muon_momentum_nesterov(const float* g, float* buf, float* u, int64_t numel, 
     return ok();
 }
 
+static_assert(muon::kMaxMomentumGroup == MUON_NESTEROV_MAX_GROUP, "grouped momentum pass size");
+
+int muon_momentum_nesterov_grouped(const float* const* g, float* const* buf, float* const* u, const int64_t* numel,
+                                   int64_t count, float mu, void* stream) {
+    using namespace muon;
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count must be >= 0 (got %lld)", (long long)count);
+    if (count == 0) return ok();
+    if (!g || !buf || !u || !numel) return fail(MUON_ERR_INVALID_ARG, "null array argument");
+    for (int64_t i = 0; i < count; ++i) {
+        if (numel[i] < 0)
+            return fail(MUON_ERR_INVALID_ARG, "numel[%lld] must be >= 0 (got %lld)", (long long)i,
+                        (long long)numel[i]);
+        if (numel[i] > 0 && (!g[i] || !buf[i] || !u[i]))
+            return fail(MUON_ERR_INVALID_ARG, "null pointer at index %lld", (long long)i);
+        if (numel[i] > 0 && u[i] == buf[i])
+            return fail(MUON_ERR_INVALID_ARG, "u must not alias buf (index %lld)", (long long)i);
+    }
+    (void)hipGetLastError();
+    // passes of up to kMaxMomentumGroup non-empty matrices, one launch each
+    MomentumGroup t{};
+    int n = 0;
+    int64_t longest = 0;
+    for (int64_t i = 0; i <= count; ++i) {
+        if (i < count && numel[i] > 0) {
+            t.g[n] = g[i];
+            t.buf[n] = buf[i];
+            t.u[n] = u[i];
+            t.numel[n] = numel[i];
+            longest = numel[i] > longest ? numel[i] : longest;
+            ++n;
+        }
+        if (n > 0 && (n == kMaxMomentumGroup || i == count)) {
+            hipError_t e = launch_momentum_grouped(t, n, longest, mu, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "grouped momentum launch");
+            n = 0;
+            longest = 0;
+        }
+    }
+    return ok();
+}
+
 size_t muon_ns5_workspace_size(int64_t rows, int64_t cols, int64_t count) {
     using namespace muon;
     if (rows < 1 || cols < 1 || count < 1) return 0;

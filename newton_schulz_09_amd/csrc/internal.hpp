@@ -92,6 +92,18 @@ struct GemmLaunch {
 hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, float mu,
                            hipStream_t stream);
 
+// Grouped momentum: up to kMaxMomentumGroup matrices per launch (one grid row
+// each), passed by value in the kernel arguments.
+constexpr int kMaxMomentumGroup = 64;
+struct MomentumGroup {
+    const float* g[kMaxMomentumGroup];
+    float* buf[kMaxMomentumGroup];
+    float* u[kMaxMomentumGroup];
+    int64_t numel[kMaxMomentumGroup];
+};
+hipError_t launch_momentum_grouped(const MomentumGroup& t, int count, int64_t max_numel, float mu,
+                                   hipStream_t stream);
+
 // One chunk of a batched norm pass: workgroups [first_block, first_block +
 // cnt * nb) of the launch; matrix i of the chunk is entry ptr_base + i of the
 // launch's pointer tables.

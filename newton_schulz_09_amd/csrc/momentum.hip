@@ -64,6 +64,40 @@ __global__ __launch_bounds__(kThreads) void k_momentum_scalar(const float* g, fl
     }
 }
 
+// Grouped form: matrix blockIdx.y of the table, the same update; 16-byte
+// groups where its three pointers are aligned, then a scalar tail.
+__global__ __launch_bounds__(kThreads) void k_momentum_grouped(MomentumGroup t, float mu) {
+    const int k = blockIdx.y;
+    const float* g = t.g[k];
+    float* buf = t.buf[k];
+    float* u = t.u[k];
+    const int64_t numel = t.numel[k];
+    const bool aligned = ((reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(buf) |
+                           reinterpret_cast<uintptr_t>(u)) & 15u) == 0;
+    const int64_t n4 = aligned ? numel / 4 : 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    for (int64_t i = first; i < n4; i += stride) {
+        const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + i);
+        f32x4 bv = reinterpret_cast<const f32x4*>(buf)[i], uv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float b = bv[q], w;
+            nesterov1(gv[q], b, w, mu);
+            bv[q] = b;
+            uv[q] = w;
+        }
+        reinterpret_cast<f32x4*>(buf)[i] = bv;
+        __builtin_nontemporal_store(uv, reinterpret_cast<f32x4*>(u) + i);
+    }
+    for (int64_t i = 4 * n4 + first; i < numel; i += stride) {
+        float b = buf[i], uv;
+        nesterov1(g[i], b, uv, mu);
+        buf[i] = b;
+        u[i] = uv;
+    }
+}
+
 inline int grid_for(int64_t work_items, int per_block) {
     int64_t blocks = (work_items + per_block - 1) / per_block;
     if (blocks > 4096) blocks = 4096;
@@ -91,6 +125,17 @@ hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, 
         k_momentum_scalar<<<grid_for(numel - done, kThreads), kThreads, 0, stream>>>(g, buf, u, done,
                                                                                     numel, mu);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_momentum_grouped(const MomentumGroup& t, int count, int64_t max_numel, float mu,
+                                  hipStream_t stream) {
+    // about 4 float4 groups per thread for the largest matrix, at most 2048
+    // workgroups per matrix
+    const int bx = grid_for((max_numel + 15) / 16, kThreads) < 2048 ? grid_for((max_numel + 15) / 16, kThreads)
+                                                                   : 2048;
+    k_momentum_grouped<<<dim3(static_cast<unsigned>(bx), static_cast<unsigned>(count)), kThreads, 0, stream>>>(t,
+                                                                                                             mu);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ CUBIC_COEFFS = (1.5, -0.5, 0.0)
 MAX_GROUP = 128
 
 #: Every symbol include/muon.h declares.
-EXPORTS = ("muon_momentum_nesterov", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
+EXPORTS = ("muon_momentum_nesterov", "muon_momentum_nesterov_grouped", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
            "muon_ns5_batched_bf16", "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
            "muon_ns5_batched_timed", "muon_newton_schulz_f32_workspace_size", "muon_newton_schulz_f32_batched",
@@ -49,6 +49,9 @@ def _load():
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     lib.muon_momentum_nesterov.argtypes = [vp, vp, vp, i64, ctypes.c_float, vp]
     lib.muon_momentum_nesterov.restype = ctypes.c_int
+    lib.muon_momentum_nesterov_grouped.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                   ctypes.POINTER(i64), i64, ctypes.c_float, vp]
+    lib.muon_momentum_nesterov_grouped.restype = ctypes.c_int
     lib.muon_ns5_workspace_size.argtypes = [i64, i64, i64]
     lib.muon_ns5_workspace_size.restype = sz
     lib.muon_ns5.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_float, vp, sz, vp]
@@ -133,6 +136,34 @@ def momentum_nesterov(g, buf, u=None, mu=0.95):
     _check(lib.muon_momentum_nesterov(g.data_ptr(), buf.data_ptr(), u.data_ptr(), g.numel(), float(mu),
                                       _stream_handle(g.device)))
     return u
+
+
+def momentum_nesterov_grouped(gs, bufs, us=None, mu=0.95):
+    """Nesterov momentum on lists of float32 tensors (one launch per 64 of
+    them): ``bufs`` are updated in place and ``us`` (new tensors unless
+    given; ``us[i]`` may be ``gs[i]``) receive the momentum outputs."""
+    gs, bufs = list(gs), list(bufs)
+    if len(bufs) != len(gs):
+        raise ValueError("bufs must match gs in length")
+    us = [torch.empty_like(g) for g in gs] if us is None else list(us)
+    if len(us) != len(gs):
+        raise ValueError("us must match gs in length")
+    if not gs:
+        return us
+    for i, (g, b, u) in enumerate(zip(gs, bufs, us)):
+        for t, name in ((g, "gs"), (b, "bufs"), (u, "us")):
+            _require_f32_cuda(t, f"{name}[{i}]")
+        if b.numel() != g.numel() or u.numel() != g.numel():
+            raise ValueError(f"entry {i}: gs, bufs and us must match in size")
+        if any(t.device != gs[0].device for t in (g, b, u)):
+            raise ValueError("all tensors must be on one device")
+    n = len(gs)
+    vp = ctypes.c_void_p
+    arr = lambda ts: (vp * n)(*[t.data_ptr() for t in ts])  # noqa: E731
+    numel = (ctypes.c_int64 * n)(*[g.numel() for g in gs])
+    _check(lib.muon_momentum_nesterov_grouped(arr(gs), arr(bufs), arr(us), numel, n, float(mu),
+                                              _stream_handle(gs[0].device)))
+    return us
 
 
 def workspace_size(rows, cols, count=1):

@@ -265,3 +265,26 @@ def test_f32_validation_errors_before_any_launch(muon):
     assert call(g, null_o, rows, cols, 2, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
     big = (i64 * 1)(20000)
     assert call(g, o, big, big, 1, 5, None, 1e-7, ws, need, None) == muon.MUON_ERR_UNSUPPORTED
+
+
+def test_grouped_momentum_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    g = (vp * 2)(0x100000, 0x100100)
+    b = (vp * 2)(0x200000, 0x200100)
+    u = (vp * 2)(0x300000, 0x300100)
+    n = (i64 * 2)(16, 7)
+    call = lib.muon_momentum_nesterov_grouped
+    assert call(None, None, None, None, 0, 0.95, None) == muon.MUON_OK          # nothing to do
+    assert call(g, b, u, n, -1, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(None, b, u, n, 2, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, u, None, 2, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, u, (i64 * 2)(16, -3), 2, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"numel[1]" in lib.muon_last_error()
+    assert call(g, b, (vp * 2)(0x300000, 0x200100), n, 2, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"alias" in lib.muon_last_error()
+    assert call((vp * 2)(0x100000, None), b, u, n, 2, 0.95, None) == muon.MUON_ERR_INVALID_ARG
+    # an empty entry may carry null pointers; with every entry empty nothing is launched
+    assert call((vp * 2)(None, None), (vp * 2)(None, None), (vp * 2)(None, None), (i64 * 2)(0, 0), 2, 0.95,
+                None) == muon.MUON_OK
