@@ -139,3 +139,18 @@ def test_gpt2_124m_set_sampled(muon):
             continue
         seen.add(shape)
         check(parity.to_np(outs[k]), oracle.ns5(it[2], precision="f32"), f"124M {shape} #{k}")
+
+
+def test_passes_over_one_workspace(muon):
+    """130 same-shaped matrices plus another shape: passes of at most 128 that
+    reuse the workspace from its start, each matrix as in a call of its own."""
+    rng = np.random.default_rng(99)
+    shapes = [(40, 96)] * 130 + [(96, 40)] * 2
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = muon.newton_schulz_f32(Gs)
+    for k in (0, 127, 128, 129, 130, 131):
+        single = parity.to_np(muon.newton_schulz_f32([Gs[k]])[0])
+        assert np.array_equal(parity.to_np(outs[k]), single), k
+    for k in (129, 131):
+        check(parity.to_np(outs[k]), oracle.ns5(host[k], precision="f32"), f"pass {k}")
