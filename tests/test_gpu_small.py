@@ -474,3 +474,19 @@ def test_momentum_grouped_ragged_misaligned_and_passes(muon):
         assert parity.ulp_diff32(parity.to_np(us[k]), want_u).max(initial=0) <= 1, k
         if o:
             assert parity.to_np(bd[k])[:o].tolist() == bh[k][:o].tolist()
+
+
+def test_large_matrices_deterministic_and_equal_single_calls(muon):
+    """m >= 2048 (256 tiles throughout): the result is the same on every call
+    and for every batch a matrix is part of, and matches the oracle."""
+    shapes = [(2048, 2048), (2048, 2304), (2304, 2048), (2048, 2048)]
+    rng = np.random.default_rng(2048)
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = [parity.to_np(o) for o in muon.ns5_batched(Gs)]
+    again = [parity.to_np(o) for o in muon.ns5_batched(Gs)]
+    for a, b in zip(outs, again):
+        assert np.array_equal(a, b)
+    _bitwise_equal_to_single(muon, Gs[:3], [cuda(o) for o in outs[:3]])
+    parity.assert_ns5_parity(outs[0], oracle.ns5(host[0]), "2048x2048")
+    parity.assert_ns5_parity(outs[2], oracle.ns5(host[2]), "2304x2048")
