@@ -71,8 +71,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "770c510eab8dfa01b1b8a704cb268363dbfc2e981eca34d8e98f0a4d025e93ef",
-    "fetch_bytes": 389610656,
+    "sources_sha256": "3f743423fa3c7ea043dcc2a977310cee84e7d8d456ae1d18f49924b2b15bc3f9",
+    "fetch_bytes": 388611924,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",

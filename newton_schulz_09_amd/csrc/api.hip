@@ -725,11 +725,12 @@ int run_f32(const float* const* G, float* const* out, const int64_t* rows, const
             sc.cols = static_cast<int>(pl.cols);
             sc.tall = pl.tall ? 1 : 0;
             sc.eps = eps;
+            sc.cnt = cnt;
             if (steps == 0) {  // X0 itself, in G's orientation
                 sc.to_out = 1;
                 sc.tiles_c = static_cast<int>((pl.cols + 31) / 32);
                 sc.tiles_per_mat = static_cast<int>((pl.rows + 31) / 32) * sc.tiles_c;
-                e = launch_f32_scale(sc, sc.tiles_per_mat * cnt, gt, &ot, stream);
+                e = launch_f32_scale(sc, gt, &ot, stream);
                 if (e != hipSuccess) return hip_fail(e, "float32 scale launch");
                 start += cnt;
                 continue;
@@ -740,7 +741,7 @@ int run_f32(const float* const* G, float* const* out, const int64_t* rows, const
             sc.ldx = pl.ldx;
             sc.tiles_c = pl.np / 32;
             sc.tiles_per_mat = (pl.mp / 32) * sc.tiles_c;
-            e = launch_f32_scale(sc, sc.tiles_per_mat * cnt, gt, nullptr, stream);
+            e = launch_f32_scale(sc, gt, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "float32 scale launch");
             const int tm = pl.mp / kF32Tile, tn = pl.np / kF32Tile;
             const int64_t xe = static_cast<int64_t>(pl.mp) * pl.ldx, ae = static_cast<int64_t>(pl.mp) * pl.lda;

@@ -18,6 +18,8 @@
 // tiles, 4 waves of 64 x 64 (2 x 2 fragments of 32 x 32), K steps of 16
 // staged k-major in LDS through registers (the next step's global loads are
 // in flight while the current one is multiplied), several workgroups per CU.
+#include <stdlib.h>
+
 #include "internal.hpp"
 
 namespace muon {
@@ -28,6 +30,7 @@ constexpr int FT = 128;        // output tile
 constexpr int FK = 16;         // K step
 constexpr int FLD = FT + 4;    // LDS row length (floats): k-major rows of 128 plus 4
 constexpr int FT_THREADS = 256;
+constexpr int64_t kMaxF32ScaleBlocks = int64_t{1} << 20;  // scale workgroups per launch
 
 // MFMA v_mfma_f32_32x32x2_f32 operand layout: lane l supplies A[l % 32][l / 32]
 // of the 32 x 2 left operand and B[l / 32][l % 32] of the 2 x 32 right one;
@@ -179,63 +182,67 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
 }
 
 // X0 = fl32(G / d) with d = sqrt(sum of the matrix's float64 partials) + eps,
-// the quotient formed in float64.  32 x 32 tiles of 32 x 8 threads.  Into the
-// workspace (X's padded extent, zeros outside G, transposed through LDS when
-// G is tall), or (to_out) straight into the outputs in G's orientation.
+// the quotient formed in float64.  32 x 32 tiles of 32 x 8 threads, taken
+// grid-stride (the grid is capped so that the largest shapes fit a launch).
+// Into the workspace (X's padded extent, zeros outside G, transposed through
+// LDS when G is tall), or (to_out) straight into the outputs in G's
+// orientation.
 __global__ __launch_bounds__(FT_THREADS) void k_f32_scale(F32Scale s, ConstPtrTable G, PtrTable out) {
-    const int b = static_cast<int>(blockIdx.x);
-    const int mat = b / s.tiles_per_mat;
-    const int t = b - mat * s.tiles_per_mat;
-    const int ti = t / s.tiles_c, tj = t - ti * s.tiles_c;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
     __shared__ double dsh;
     __shared__ float tl[32][33];
-    if (threadIdx.x == 0) {  // fixed order: every workgroup of a matrix gets the same d
-        const double* pp = s.partials + static_cast<int64_t>(mat) * s.nb;
-        double acc = 0.0;
-        for (int p = 0; p < s.nb; ++p) acc += pp[p];
-        dsh = sqrt(acc) + static_cast<double>(s.eps);
-    }
-    __syncthreads();
-    const double d = dsh;
-    const float* g = G.p[mat];
-    const int i0 = ti * 32, j0 = tj * 32;
-    if (s.to_out) {  // rows x cols, no padding, no transpose
-        float* o = out.p[mat];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int i = i0 + ty + 8 * rr, j = j0 + tx;
-            if (i < s.rows && j < s.cols)
-                o[static_cast<int64_t>(i) * s.cols + j] =
-                    static_cast<float>(static_cast<double>(g[static_cast<int64_t>(i) * s.cols + j]) / d);
-        }
-        return;
-    }
-    float* X = s.X + static_cast<int64_t>(mat) * s.x_mat;
-    const int m = s.tall ? s.cols : s.rows, n = s.tall ? s.rows : s.cols;
-    if (!s.tall) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int i = i0 + ty + 8 * rr, j = j0 + tx;
-            const float v = (i < m && j < n)
-                                ? static_cast<float>(static_cast<double>(g[static_cast<int64_t>(i) * s.cols + j]) / d)
-                                : 0.0f;
-            X[static_cast<int64_t>(i) * s.ldx + j] = v;
-        }
-    } else {
-        // X[i][j] = G[j][i]: read the G tile along its rows, write X along its
-        // rows
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int jj = j0 + ty + 8 * rr, ii = i0 + tx;
-            tl[ty + 8 * rr][tx] = (jj < n && ii < m) ? g[static_cast<int64_t>(jj) * s.cols + ii] : 0.0f;
+    const int64_t total = static_cast<int64_t>(s.tiles_per_mat) * s.cnt;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int mat = static_cast<int>(b / s.tiles_per_mat);
+        const int t = static_cast<int>(b - static_cast<int64_t>(mat) * s.tiles_per_mat);
+        const int ti = t / s.tiles_c, tj = t - ti * s.tiles_c;
+        __syncthreads();  // the previous tile is done with dsh and tl
+        if (threadIdx.x == 0) {  // fixed order: every tile of a matrix gets the same d
+            const double* pp = s.partials + static_cast<int64_t>(mat) * s.nb;
+            double acc = 0.0;
+            for (int p = 0; p < s.nb; ++p) acc += pp[p];
+            dsh = sqrt(acc) + static_cast<double>(s.eps);
         }
         __syncthreads();
+        const double d = dsh;
+        const float* g = G.p[mat];
+        const int i0 = ti * 32, j0 = tj * 32;
+        if (s.to_out) {  // rows x cols, no padding, no transpose
+            float* o = out.p[mat];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int i = i0 + ty + 8 * rr, j = j0 + tx;
-            X[static_cast<int64_t>(i) * s.ldx + j] =
-                static_cast<float>(static_cast<double>(tl[tx][ty + 8 * rr]) / d);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = i0 + ty + 8 * rr, j = j0 + tx;
+                if (i < s.rows && j < s.cols)
+                    o[static_cast<int64_t>(i) * s.cols + j] =
+                        static_cast<float>(static_cast<double>(g[static_cast<int64_t>(i) * s.cols + j]) / d);
+            }
+            continue;
+        }
+        float* X = s.X + static_cast<int64_t>(mat) * s.x_mat;
+        const int m = s.tall ? s.cols : s.rows, n = s.tall ? s.rows : s.cols;
+        if (!s.tall) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = i0 + ty + 8 * rr, j = j0 + tx;
+                const float v =
+                    (i < m && j < n) ? static_cast<float>(static_cast<double>(g[static_cast<int64_t>(i) * s.cols + j]) / d)
+                                     : 0.0f;
+                X[static_cast<int64_t>(i) * s.ldx + j] = v;
+            }
+        } else {
+            // X[i][j] = G[j][i]: read the G tile along its rows, write X along
+            // its rows
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int jj = j0 + ty + 8 * rr, ii = i0 + tx;
+                tl[ty + 8 * rr][tx] = (jj < n && ii < m) ? g[static_cast<int64_t>(jj) * s.cols + ii] : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = i0 + ty + 8 * rr, j = j0 + tx;
+                X[static_cast<int64_t>(i) * s.ldx + j] = static_cast<float>(static_cast<double>(tl[tx][ty + 8 * rr]) / d);
+            }
         }
     }
 }
@@ -255,11 +262,20 @@ hipError_t launch_f32_gemm(GemmKind kind, const F32Gemm& g, int blocks, const Pt
     return hipGetLastError();
 }
 
-hipError_t launch_f32_scale(const F32Scale& s, int blocks, const ConstPtrTable& G, const PtrTable* out,
-                            hipStream_t stream) {
+hipError_t launch_f32_scale(const F32Scale& s, const ConstPtrTable& G, const PtrTable* out, hipStream_t stream) {
     PtrTable o{};
     if (out) o = *out;
-    k_f32_scale<<<blocks, FT_THREADS, 0, stream>>>(s, G, o);
+    // the kernel walks s.tiles_per_mat * s.cnt tiles grid-stride
+    // MUON_F32_SCALE_WG_CAP=n lowers the cap (read at every call; for tests
+    // of the several-tiles path, which only very large inputs reach otherwise)
+    int64_t cap = kMaxF32ScaleBlocks;
+    if (const char* e = getenv("MUON_F32_SCALE_WG_CAP")) {
+        const long long v = atoll(e);
+        if (v >= 1 && v < cap) cap = v;
+    }
+    const int64_t total = static_cast<int64_t>(s.tiles_per_mat) * s.cnt;
+    const int64_t grid = total < cap ? total : cap;
+    k_f32_scale<<<static_cast<unsigned>(grid), FT_THREADS, 0, stream>>>(s, G, o);
     return hipGetLastError();
 }
 

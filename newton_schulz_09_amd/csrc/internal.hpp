@@ -203,10 +203,10 @@ struct F32Scale {
     int64_t x_mat;
     int ldx;
     int tiles_c, tiles_per_mat;
+    int cnt;  // matrices
     int to_out;
     float eps;
 };
-hipError_t launch_f32_scale(const F32Scale& s, int blocks, const ConstPtrTable& G, const PtrTable* out,
-                            hipStream_t stream);
+hipError_t launch_f32_scale(const F32Scale& s, const ConstPtrTable& G, const PtrTable* out, hipStream_t stream);
 
 }  // namespace muon
