@@ -76,7 +76,7 @@ COPY_BYTES = 1 << 30
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
     "sources_sha256": "3f743423fa3c7ea043dcc2a977310cee84e7d8d456ae1d18f49924b2b15bc3f9",
-    "fetch_bytes": 388611924,
+    "fetch_bytes": 387394149,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
