@@ -15,10 +15,12 @@
 // fragments are formed with gfx950's transposing LDS reads
 // (ds_read_b64_tr_b16), so X is never stored transposed.
 //
-// Engine (gfx950): WGM x WGN wavefronts of 64 lanes (2x2 for square tiles;
-// 4x2 for the 256x128 tile of a X + B X), each owning a (BM/WGM)x(BN/WGN)
-// sub-tile built from 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, fp32
-// accumulation).  K advances
+// Engine (gfx950): WGM x WGN wavefronts of 64 lanes, each owning a
+// (BM/WGM)x(BN/WGN) sub-tile built from 32x32 MFMA fragments
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  The 256x256 tiles of
+// a X + B X and of X X^T run on 2x4 waves (two per SIMD; a symmetric
+// product's diagonal tiles then go in 64x64 blocks), the other square tiles
+// on 2x2, the 256x128 tile of a X + B X on 4x2.  K advances
 // BK at a time through a ring of STAGES LDS buffers filled by direct
 // global->LDS loads (global_load_lds_dwordx4: each lane supplies a global
 // address, the 64 lanes' 16-byte pieces land contiguously in LDS), so the
@@ -36,13 +38,17 @@
 //
 // Work distribution: one workgroup per output tile, every matrix of every
 // segment (a set of same-shaped matrices; up to kMaxSeg shapes that share the
-// tile size) in the same launch.  Consecutive workgroups are dispatched round-robin over
-// the 8 XCDs (each with its own L2), so the workgroup index is remapped to
-// give every XCD a contiguous range of tiles; within a matrix, tiles of the
-// full grid are ordered in bands of `band` tile rows, column by column inside
-// a band, so that the tiles resident on one XCD share operand panels (with
-// all tile rows in one band, each column panel of the second operand is read
-// from memory once).
+// tile size) in the same launch.  Consecutive workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2), so the workgroup index
+// is remapped: for the full grid (a X + B X) every XCD takes a contiguous
+// range of tiles, and within a matrix tiles are ordered in bands of `band`
+// tile rows, column by column inside a band, so that the tiles resident on
+// one XCD share operand panels (with all tile rows in one band, each column
+// panel of the second operand is read from memory once); for the symmetric
+// products, whose K differs between segments, whole matrices are dealt to
+// the XCDs in turn.  The mapping only places work: every output element is
+// accumulated in the same K order under any tile shape or mapping, so a
+// matrix gets bitwise the same result in any batch.
 #include <stdlib.h>
 
 #include <type_traits>

@@ -163,7 +163,8 @@ hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const 
                            bool apply = false, float lr = 0.0f, bool out16 = false);
 
 // One GEMM launch of `blocks` workgroups with tile x tile_n output tiles:
-// square tiles of 64, 128 or 256 for every kind, and 256 x 128 for a X + B X.
+// square tiles of 64, 128 or 256 for every kind, and 256 x 128 or 192 x 256
+// for a X + B X.
 hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& launch, int blocks,
                        const PtrTable* out, hipStream_t stream);
 
