@@ -110,6 +110,37 @@ int64_t max_cast_workgroups() {
 
 }  // namespace
 
+// Tile of the symmetric products.  With 256 tiles (m >= 2048) a pass has
+// cnt T (T + 1) / 2 upper tiles, one workgroup per CU each: at m = 4096 that
+// is 136 for 256 CUs, a single round that leaves almost half of them idle.
+// 192 tiles on m rounded up to 192 give more, smaller tiles (253 at m =
+// 4096).  They are taken when both tilings fit in one round of the 256 CUs:
+// the round then lasts one 192 tile, about 0.56 of a 256 tile's work (0.66
+// of its time at the measured lower speed per flop of the smaller tile).
+// Past one round the smaller tiles' extra rounds cost more than they save, so
+// the 256 tiles stay.  The padding stays zero, and every element is
+// accumulated in the same K order under either tile.  MUON_SYM_TILE=256 (or
+// 192, where it covers mp) forces the choice for m >= 2048.
+void choose_sym_tile(Ns5Plan* p) {
+    p->sym_tile = p->tile;
+    p->msym = p->mp;
+    if (p->tile != 256) return;
+    static const int forced = [] {
+        const char* s = getenv("MUON_SYM_TILE");
+        const int t = s ? atoi(s) : 0;
+        return (t == 192 || t == 256) ? t : 0;
+    }();
+    const int m192 = static_cast<int>(round_up(p->m, 192));
+    if (forced == 256 || m192 < p->mp) return;  // the 192 padding must cover mp
+    constexpr int64_t kCus = 256;
+    const int64_t t256 = p->mp / 256, t192 = m192 / 192;
+    const bool one_round = p->cnt * t256 * (t256 + 1) / 2 <= kCus && p->cnt * t192 * (t192 + 1) / 2 <= kCus;
+    if (forced == 192 || one_round) {
+        p->sym_tile = 192;
+        p->msym = m192;
+    }
+}
+
 bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* p) {
     if (rows < 1 || cols < 1 || count < 1) return false;
     const int64_t m = rows < cols ? rows : cols;
@@ -130,10 +161,11 @@ bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* p) {
     if (cnt * bx_tiles > kMaxWorkgroups) cnt = kMaxWorkgroups / bx_tiles;
     if (cnt < 1) return false;
     p->cnt = static_cast<int>(cnt);
+    choose_sym_tile(p);
     p->ldx = p->np + ld_skew();
-    p->lda = p->mp + ld_skew();
-    p->x_elems = static_cast<size_t>(p->mp) * p->ldx;
-    p->a_elems = static_cast<size_t>(p->mp) * p->lda;
+    p->lda = p->msym + ld_skew();
+    p->x_elems = static_cast<size_t>(p->msym) * p->ldx;
+    p->a_elems = static_cast<size_t>(p->msym) * p->lda;
     size_t off = 0;
     const size_t xb = align256(cnt * p->x_elems * sizeof(bf16_t));
     const size_t ab = align256(cnt * p->a_elems * sizeof(bf16_t));
@@ -199,7 +231,8 @@ int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups) {
                 return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits",
                             (long long)sg.rows, (long long)sg.cols);
             Group* g = groups->empty() ? nullptr : &groups->back();
-            if (!g || g->tile != pl.tile || g->mats + pl.cnt > kMaxGroup ||
+            if (!g || g->tile != pl.tile || g->chunks[0].plan.sym_tile != pl.sym_tile ||
+                g->mats + pl.cnt > kMaxGroup ||
                 static_cast<int>(g->chunks.size()) == kMaxSeg || g->bx_blocks + bx_blocks(pl) > kMaxWorkgroups) {
                 groups->emplace_back();
                 g = &groups->back();
@@ -302,8 +335,8 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
         int nb_norm = 0, nb_cast = 0;
         int64_t cast_tiles = 0;
         for (const Chunk& c : grp.chunks) {
-            const int rows_pad = c.plan.tall ? c.plan.np : c.plan.mp;
-            const int cols_pad = c.plan.tall ? c.plan.mp : c.plan.np;
+            const int rows_pad = c.plan.tall ? c.plan.np : c.plan.msym;
+            const int cols_pad = c.plan.tall ? c.plan.msym : c.plan.np;
             cast_tiles += static_cast<int64_t>(rows_pad / 64) * (cols_pad / 64) * c.plan.cnt;
         }
         // tiles per cast workgroup: cast_tiles_per_wg(), more if the grid
@@ -335,8 +368,8 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             ns.partials = b.part;
             nb_norm += pl.nb * pl.cnt;
             CastSeg& cs = cl.seg[ci];
-            const int rows_pad = pl.tall ? pl.np : pl.mp;
-            const int cols_pad = pl.tall ? pl.mp : pl.np;
+            const int rows_pad = pl.tall ? pl.np : pl.msym;
+            const int cols_pad = pl.tall ? pl.msym : pl.np;
             cs.first_block = nb_cast;
             cs.tiles_c = cols_pad / 64;
             cs.tiles_per_mat = (rows_pad / 64) * cs.tiles_c;
@@ -414,6 +447,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             bool rows256 = true;
             for (const Chunk& c : grp.chunks) rows256 = rows256 && c.plan.mp % 256 == 0;
             if (want != 128 && grp.tile == 128 && rows256) syrk_tile = 256;
+            if (grp.chunks[0].plan.sym_tile == 192) syrk_tile = 192;  // the same for every chunk of a group
         }
         int syrk_order[kMaxSeg];
         for (int ci = 0; ci < nseg; ++ci) syrk_order[ci] = ci;
@@ -423,6 +457,14 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                 syrk_order[b] = syrk_order[b - 1];
                 syrk_order[b - 1] = t;
             }
+        // X[1]'s rows past mp (the symmetric products' padding) are never
+        // written by a X + B X: they start at zero (X[0]'s by the cast)
+        for (const Chunk& c : grp.chunks) {
+            if (c.plan.msym <= c.plan.mp) continue;
+            e = launch_zero_rows(bufs_of(ws, c).X[1], static_cast<int64_t>(c.plan.x_elems), c.plan.cnt, c.plan.mp,
+                                 c.plan.msym, c.plan.ldx, stream);
+            if (e != hipSuccess) return hip_fail(e, "padding reset launch");
+        }
         int cur = 0;
         for (int s = 0; s < steps; ++s) {
             const int nxt = cur ^ 1;
@@ -434,7 +476,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                 const Chunk& c = grp.chunks[syrk_order[k]];
                 const Ns5Plan& pl = c.plan;
                 ChunkBufs b = bufs_of(ws, c);
-                const int tiles_m = pl.mp / syrk_tile;
+                const int tiles_m = pl.msym / syrk_tile;
                 const int64_t xe = static_cast<int64_t>(pl.x_elems);
                 GemmArgs& g1 = syrk.seg[k];
                 g1.first_block = nb_syrk;
@@ -451,7 +493,7 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                 const Chunk& c = grp.chunks[ci];
                 const Ns5Plan& pl = c.plan;
                 ChunkBufs b = bufs_of(ws, c);
-                const int tiles_m = pl.mp / pl.tile;
+                const int tiles_m = pl.msym / pl.sym_tile;
                 const int64_t xe = static_cast<int64_t>(pl.x_elems);
                 const int64_t ae = static_cast<int64_t>(pl.a_elems);
                 // B = b A + c A A  (the upper triangle of tiles)
@@ -494,7 +536,8 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
             }
             e = launch_gemm(GEMM_SYRK, syrk_tile, syrk_tile, syrk, nb_syrk, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
-            e = launch_gemm(GEMM_AAB, grp.tile, grp.tile, aab, nb_sym, nullptr, stream);
+            const int aab_tile = grp.chunks[0].plan.sym_tile;
+            e = launch_gemm(GEMM_AAB, aab_tile, aab_tile, aab, nb_sym, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "b A + c A A launch");
             const bool timed = sink && !last && sink->recorded < sink->pairs;
             if (timed) {

@@ -877,6 +877,18 @@ hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTab
     return hipGetLastError();
 }
 
+// The symmetric products only (for tiles no full-grid product uses).
+template <int BM, int BK, int STAGES>
+hipError_t launch_sym_t(GemmKind kind, const GemmLaunch& L, int blocks, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(blocks));
+    switch (kind) {
+        case GEMM_SYRK: k_gemm_nt<BM, BM, BK, STAGES, 2, 2, GEMM_SYRK><<<grid, 256, 0, stream>>>(L, PtrTable{}); break;
+        case GEMM_AAB: k_gemm_nt<BM, BM, BK, STAGES, 2, 2, GEMM_AAB><<<grid, 256, 0, stream>>>(L, PtrTable{}); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& launch, int blocks,
@@ -894,6 +906,9 @@ hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& la
         return launch_t<192, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
     }
     if (tile_n != tile) return hipErrorInvalidValue;
+    // 192 x 192 tiles of the symmetric products (2 x 2 waves of 96 x 96):
+    // 4224 = 22 x 192 gives 253 upper tiles where 4096 = 16 x 256 gives 136
+    if (tile == 192) return launch_sym_t<192, 64, 2>(kind, launch, blocks, stream);
     // 256 x 256 tiles of a X + B X: 8 waves (2 x 4, each 128 x 64) by default,
     // two per SIMD; MUON_BX_WAVES=4 selects the 4-wave engine (for tuning)
     static const int bx_waves = [] {

@@ -30,9 +30,15 @@ struct Ns5Plan {
     bool tall;
     int tile;
     int mp, np;
+    // tile of the symmetric products (X X^T, b A + c A A) and the padded
+    // size they run on: the group tile and mp, or for m >= 2048 possibly 192
+    // and m rounded up to 192 (>= mp), where that gives the CUs a fuller round
+    // of tiles.  X has msym rows (the rows past mp stay zero) and A, B are
+    // msym x msym.
+    int sym_tile, msym;
     int nb;    // norm partials per matrix
     int cnt;   // matrices per pass
-    // row strides (elements) of X (mp rows) and A, B (mp rows): the padded
+    // row strides (elements) of X (msym rows) and A, B (msym rows): the padded
     // widths plus a skew that keeps rows of power-of-two widths from all
     // starting on the same memory channel
     int ldx, lda;
@@ -159,6 +165,10 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
 // out[i] = float32 of X (transposed back when G is tall): the steps = 0 result.
 // apply: out[i] <- out[i] - lr * X (the parameter update) instead; out16:
 // out[i] holds bfloat16 and receives X as is.
+// Zeroes rows [first_row, rows) of each of cnt row-major bf16 matrices (ld
+// elements per row, x_mat elements apart).
+hipError_t launch_zero_rows(bf16_t* X, int64_t x_mat, int cnt, int first_row, int rows, int ld, hipStream_t stream);
+
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
                            bool apply = false, float lr = 0.0f, bool out16 = false);
 

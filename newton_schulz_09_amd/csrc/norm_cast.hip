@@ -318,6 +318,14 @@ __global__ __launch_bounds__(kThreads) void k_scale_cast(CastLaunch L, ConstPtrT
     }
 }
 
+// Zeroes n elements from `offset` of matrix blockIdx.y (x_mat apart).
+__global__ __launch_bounds__(kThreads) void k_zero_rows(bf16_t* X, int64_t x_mat, int64_t offset, int64_t n) {
+    bf16_t* p = X + static_cast<int64_t>(blockIdx.y) * x_mat + offset;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads)
+        p[i] = 0;
+}
+
 // out[i] = float32 of X in G's orientation (the steps = 0 result), with
 // `apply` the parameter update out[i] <- out[i] - lr * X instead, or with
 // `out16` X itself as bfloat16.
@@ -360,6 +368,16 @@ hipError_t launch_scale_cast(const CastLaunch& L, int blocks, const ConstPtrTabl
         k_scale_cast<true><<<blocks, kThreads, 0, stream>>>(L, G, eps);
     else
         k_scale_cast<false><<<blocks, kThreads, 0, stream>>>(L, G, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(bf16_t* X, int64_t x_mat, int cnt, int first_row, int rows, int ld, hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(rows - first_row) * ld;
+    if (n <= 0 || cnt <= 0) return hipSuccess;
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 1024) blocks = 1024;
+    k_zero_rows<<<dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(cnt)), kThreads, 0, stream>>>(
+        X, x_mat, static_cast<int64_t>(first_row) * ld, n);
     return hipGetLastError();
 }
 
