@@ -111,16 +111,18 @@ int64_t max_cast_workgroups() {
 }  // namespace
 
 // Tile of the symmetric products.  With 256 tiles (m >= 2048) a pass has
-// cnt T (T + 1) / 2 upper tiles, one workgroup per CU each: at m = 4096 that
-// is 136 for 256 CUs, a single round that leaves almost half of them idle.
-// 192 tiles on m rounded up to 192 give more, smaller tiles (253 at m =
-// 4096).  They are taken when both tilings fit in one round of the 256 CUs:
-// the round then lasts one 192 tile, about 0.56 of a 256 tile's work (0.66
-// of its time at the measured lower speed per flop of the smaller tile).
-// Past one round the smaller tiles' extra rounds cost more than they save, so
-// the 256 tiles stay.  The padding stays zero, and every element is
-// accumulated in the same K order under either tile.  MUON_SYM_TILE=256 (or
-// 192, where it covers mp) forces the choice for m >= 2048.
+// n256 = cnt T (T + 1) / 2 upper tiles, one workgroup per CU each, so it takes
+// ceil(n256 / 256) rounds of the 256 CUs: one 4096^2 matrix has 136 tiles, a
+// single round that leaves almost half of them idle; two have 272, a second
+// round of 16.  192 tiles on m rounded up to 192 give more, smaller tiles
+// (253 per 4096^2 matrix), each round lasting about 0.5625 / 0.85 of a 256
+// round (the smaller share of the work at the measured lower speed per
+// flop).  192 is taken where that predicts at least 10% less time; measured:
+// one 4096^2 1.68 -> 1.53 ms, two 3.17 -> 2.78 ms, while the 16 matrices of
+// 2048 x 8192 (9.96 against 10.44 ms) and eight of them keep 256.  The
+// padding stays zero, and every element is accumulated in the same K order
+// under any tile.  MUON_SYM_TILE=256, 192 (where it covers mp) or 128 forces
+// the choice for m >= 2048 (for tuning).
 void choose_sym_tile(Ns5Plan* p) {
     p->sym_tile = p->tile;
     p->msym = p->mp;
@@ -128,14 +130,19 @@ void choose_sym_tile(Ns5Plan* p) {
     static const int forced = [] {
         const char* s = getenv("MUON_SYM_TILE");
         const int t = s ? atoi(s) : 0;
-        return (t == 192 || t == 256) ? t : 0;
+        return (t == 128 || t == 192 || t == 256) ? t : 0;
     }();
+    if (forced == 128) {  // mp, a multiple of 256, is one of 128 too
+        p->sym_tile = 128;
+        return;
+    }
     const int m192 = static_cast<int>(round_up(p->m, 192));
     if (forced == 256 || m192 < p->mp) return;  // the 192 padding must cover mp
-    constexpr int64_t kCus = 256;
-    const int64_t t256 = p->mp / 256, t192 = m192 / 192;
-    const bool one_round = p->cnt * t256 * (t256 + 1) / 2 <= kCus && p->cnt * t192 * (t192 + 1) / 2 <= kCus;
-    if (forced == 192 || one_round) {
+    constexpr double kCus = 256.0;
+    const double t256 = p->mp / 256, t192 = m192 / 192;
+    const double rounds256 = ceil(p->cnt * t256 * (t256 + 1) / 2 / kCus);
+    const double rounds192 = ceil(p->cnt * t192 * (t192 + 1) / 2 / kCus) * 0.5625 / 0.85;
+    if (forced == 192 || rounds192 < 0.9 * rounds256) {
         p->sym_tile = 192;
         p->msym = m192;
     }

@@ -490,3 +490,15 @@ def test_large_matrices_deterministic_and_equal_single_calls(muon):
     _bitwise_equal_to_single(muon, Gs[:3], [cuda(o) for o in outs[:3]])
     parity.assert_ns5_parity(outs[0], oracle.ns5(host[0]), "2048x2048")
     parity.assert_ns5_parity(outs[2], oracle.ns5(host[2]), "2304x2048")
+
+
+def test_two_4096_matrices_equal_single_calls(muon):
+    """Two 4096 x 4096 matrices in one call (symmetric products on 192 tiles
+    over m padded to 4224, two matrices per launch) give bitwise what each
+    gets alone."""
+    g = torch.Generator(device="cuda").manual_seed(4096)
+    Gs = [torch.randn(4096, 4096, device="cuda", generator=g) for _ in range(2)]
+    outs = muon.ns5_batched(Gs)
+    for k, G in enumerate(Gs):
+        assert torch.equal(outs[k], muon.ns5(G)), k
+        assert torch.isfinite(outs[k]).all()
