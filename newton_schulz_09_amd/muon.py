@@ -27,6 +27,10 @@ NS5_EPS = 1e-7
 NS5_COEFFS = (3.4445, -4.7750, 2.0315)
 CUBIC_COEFFS = (1.5, -0.5, 0.0)
 MAX_GROUP = 128
+#: Accepted shapes (MUON_NS5_MAX_SHORT / MUON_NS5_MAX_LONG): short side <=
+#: MAX_SHORT and long side <= MAX_LONG.
+MAX_SHORT = 16384
+MAX_LONG = 1 << 20
 
 #: Every symbol include/muon.h declares.
 EXPORTS = ("muon_momentum_nesterov", "muon_momentum_nesterov_grouped", "muon_ns5_workspace_size", "muon_ns5", "muon_ns5_grouped",

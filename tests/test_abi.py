@@ -49,6 +49,20 @@ def test_workspace_size(muon):
     assert muon.workspace_size(1, 1, 1) > 0
 
 
+def test_shape_limits(muon):
+    S, L = muon.MAX_SHORT, muon.MAX_LONG
+    for rows, cols in ((S, S), (16, L), (L, 16), (S, L), (L, S)):
+        assert muon.workspace_size(rows, cols, 1) > 0, (rows, cols)
+    for rows, cols in ((S + 1, S + 1), (16, L + 1), (L + 1, 16), (S + 1, L)):
+        assert muon.workspace_size(rows, cols, 1) == 0, (rows, cols)
+    # the largest accepted shape: two copies of X (bf16, 16384 x >= 2^20) alone
+    # pass 2^36 bytes, so every size on the way is 64-bit
+    big = muon.workspace_size(S, L, 1)
+    assert big >= 2 * S * L * 2 + 2 * S * S * 2
+    assert big < 2 * (2 * S * (L + 1024) * 2 + 2 * (S + 1024) ** 2 * 2)
+    assert muon.workspace_size(S, L, 2) >= 2 * big - 256
+
+
 def test_validation_errors_before_any_launch(muon):
     lib = muon.lib
     fake = ctypes.c_void_p(0x100000)            # never dereferenced: calls fail validation first
