@@ -75,8 +75,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "66c3ba5594b8c5bbe207d1f49f6c4156876924057d1e12ed06e8c4b7f56c9c57",
-    "fetch_bytes": 388078074,
+    "sources_sha256": "e587a9b9a275f25fd2769f9c869c918be1dcfbc2f14800567ff2a1571aa3c8c0",
+    "fetch_bytes": 387012697,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",

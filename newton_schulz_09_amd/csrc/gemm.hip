@@ -839,8 +839,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                         hi[e] = fmaf(-args.lr, hi[e], phi[e]);
                     }
                 }
-                *reinterpret_cast<f32x4*>(dst) = lo;
-                *reinterpret_cast<f32x4*>(dst + 4) = hi;
+                // streaming stores: the output is never read again by this
+                // launch, and must not evict the operands its tiles share in L2
+                __builtin_nontemporal_store(lo, reinterpret_cast<f32x4*>(dst));
+                __builtin_nontemporal_store(hi, reinterpret_cast<f32x4*>(dst + 4));
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
