@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G
                     bv[q] = fmaf(mu, bv[q], gv[q]);
                     u[q] = fmaf(mu, bv[q], gv[q]);
                 }
-                *reinterpret_cast<f32x4*>(buf + i) = bv;
+                __builtin_nontemporal_store(bv, reinterpret_cast<f32x4*>(buf + i));
                 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
                 *reinterpret_cast<u32x2v*>(u16 + i) =
                     u32x2v{f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3])};
@@ -124,12 +124,15 @@ __global__ __launch_bounds__(kThreads) void k_norm(NormLaunch L, ConstPtrTable G
         for (int64_t i = begin + 4 * static_cast<int64_t>(threadIdx.x); i < end; i += 8 * kThreads) {
             const int64_t i2 = i + 4 * kThreads;
             const bool two = i2 < end;
+            // g and buf are touched once per step: they stream past the caches
+            // (non-temporal), which then keep the staging copy written here
+            // and the X the cast writes from it for the first X X^T
             const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
             f32x4 bv{}, gv2{}, bv2{};
-            if constexpr (MOM) bv = *reinterpret_cast<const f32x4*>(buf + i);
+            if constexpr (MOM) bv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(buf + i));
             if (two) {
                 gv2 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i2));
-                if constexpr (MOM) bv2 = *reinterpret_cast<const f32x4*>(buf + i2);
+                if constexpr (MOM) bv2 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(buf + i2));
             }
             step4(i, gv, bv);
             if (two) step4(i2, gv2, bv2);
@@ -177,8 +180,8 @@ __device__ __forceinline__ void cast_load(const float* g, const bf16_t* u16, int
         const int idx = threadIdx.x + h * kThreads;
         const int gr = r0 + (idx >> 3), gc = c0 + (idx & 7) * 8;
         if (gr < rows && vec && gc + 8 <= cols) {
-            if constexpr (BF16IN) {
-                const u32x4v w = *reinterpret_cast<const u32x4v*>(u16 + static_cast<int64_t>(gr) * cols + gc);
+            if constexpr (BF16IN) {  // read once: streamed
+                const u32x4v w = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(u16 + static_cast<int64_t>(gr) * cols + gc));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[h][2 * e] = bf16_to_f32(static_cast<bf16_t>(w[e] & 0xffffu));
