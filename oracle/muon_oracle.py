@@ -14,7 +14,8 @@ Source: Synced (机器之心) report on Modded-NanoGPT, section "Muon optimizer"
   * the summary paragraph that follows says momentum is Nesterov's and that
     orthogonalisation comes after it, and that the iteration runs in bfloat16.
 
-Arithmetic contract (the readings are listed in DESIGN.md, "Readings"):
+Arithmetic contract (where the section is silent, the plainest reading the
+rest of it supports):
   * every sum and product is carried in float64 (exact for the bf16 x bf16
     products, ~1e-16 relative for the sums);
   * a value is rounded straight from float64 to bfloat16 (round to nearest,
