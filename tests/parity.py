@@ -49,6 +49,27 @@ def assert_ns5_parity(got, want, name="", check_sigma=True):
     return r
 
 
+#: Bar of the iteration carried in float32 against the oracle's float32
+#: iteration: the GPU accumulates the products in float32 (MFMA), the oracle in
+#: float64, which alone lands 0.5e-6 .. 3.3e-6 apart (numpy, float32 against
+#: float64 accumulation), so the bar leaves a 30-fold margin and is 100 times
+#: tighter than the distance between the bf16 and float32 iterations.
+F32_REL_FRO_TOL = 1e-4
+F32_SIGMA_TOL = 1e-4
+
+
+def assert_f32_parity(got, want, name=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    r = rel_fro(got, want)
+    assert r <= F32_REL_FRO_TOL, f"{name}: relative Frobenius error {r:.3g} > {F32_REL_FRO_TOL}"
+    d = np.max(np.abs(svals(got) - svals(want)))
+    assert d <= F32_SIGMA_TOL, f"{name}: singular values differ by {d:.3g} > {F32_SIGMA_TOL}"
+    return r
+
+
 def ulp_diff32(a, b):
     a = np.ascontiguousarray(a, dtype=np.float32)
     b = np.ascontiguousarray(b, dtype=np.float32)

@@ -29,3 +29,12 @@ def test_off_block_check_sees_a_stray_entry():
     r, c = rows[0][0], cols[1][0]
     G[r, c] = 1e-30
     assert not blockdiag.off_block_is_zero(G, rows, cols)
+
+
+def test_whole_matrix_equals_augmented_blocks_float32_iteration():
+    G, rows, cols, blocks = blockdiag.permuted_block_diagonal(96, 3, seed=5)
+    O = oracle.ns5(G, precision="f32")
+    assert blockdiag.off_block_is_zero(O, rows, cols)
+    for b in range(3):
+        Ob = oracle.ns5(blockdiag.augmented(blocks, b), precision="f32")[:32, :32]
+        assert parity.rel_fro(O[np.ix_(rows[b], cols[b])], Ob) <= 1e-5, b

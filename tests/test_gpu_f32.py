@@ -20,9 +20,6 @@ from . import parity
 
 pytestmark = pytest.mark.gpu
 
-REL = 1e-4
-SIG = 1e-4
-
 
 @pytest.fixture(scope="module")
 def muon():
@@ -37,14 +34,7 @@ def cuda(a):
 
 
 def check(got, want, name):
-    got = np.asarray(got, dtype=np.float64)
-    want = np.asarray(want, dtype=np.float64)
-    assert got.shape == want.shape, name
-    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
-    r = parity.rel_fro(got, want)
-    assert r <= REL, f"{name}: relative Frobenius error {r:.3g} > {REL}"
-    d = np.max(np.abs(parity.svals(got) - parity.svals(want)))
-    assert d <= SIG, f"{name}: singular values differ by {d:.3g} > {SIG}"
+    parity.assert_f32_parity(got, want, name)
 
 
 SHAPES = [(1, 1), (3, 5), (5, 3), (64, 64), (65, 130), (130, 65), (100, 1000), (257, 300), (640, 700),
