@@ -30,6 +30,7 @@ constexpr int FT = 128;        // output tile
 constexpr int FK = 16;         // K step
 constexpr int FLD = FT + 4;    // LDS row length (floats): k-major rows of 128 plus 4
 constexpr int FT_THREADS = 256;
+constexpr int kFKBlock = 64;   // K steps (of FK) per block of the two-level sum: 1024 K values
 constexpr int64_t kMaxF32ScaleBlocks = int64_t{1} << 20;  // scale workgroups per launch
 
 // MFMA v_mfma_f32_32x32x2_f32 operand layout: lane l supplies A[l % 32][l / 32]
@@ -106,13 +107,19 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
         }
     };
 
-    f32x16 acc[2][2];
+    // Two-level sum: the matrix cores accumulate one block of kFKBlock K
+    // steps (1024 K values) at a time into `acc`, and each block's sum is
+    // added to `tot` with one float32 rounding, block after block.  The
+    // matrix cores' accumulator drifts from a round-to-nearest sum by an
+    // amount that grows with the number of terms it carries, so capping that
+    // number keeps a long K as close to the float64 sum as a short one.
+    f32x16 acc[2][2], tot[2][2];
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[fm][fn][r] = tot[fm][fn][r] = 0.0f;
 
     const int nk = g.K / FK;
     gload(0);
@@ -137,6 +144,17 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm], bq[fn], acc[fm][fn], 0, 0, 0);
         }
         if (kt + 1 < nk) lstore(cur ^ 1);
+        if ((kt + 1) % kFKBlock == 0 || kt + 1 == nk) {  // close the block
+#pragma unroll
+            for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        tot[fm][fn][r] += acc[fm][fn][r];
+                        acc[fm][fn][r] = 0.0f;
+                    }
+        }
         __syncthreads();
     }
 
@@ -153,7 +171,7 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
             for (int r = 0; r < 16; ++r) {
                 const int i = i0 + wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
                 const int j = j0 + wn * 64 + fn * 32 + fr;
-                float v = acc[fm][fn][r];
+                float v = tot[fm][fn][r];
                 if constexpr (KIND == GEMM_SYRK) {
                     // upper tiles hold (i, j) and its mirror; a diagonal tile
                     // writes i <= j only, so A is exactly symmetric
@@ -266,13 +284,14 @@ hipError_t launch_f32_scale(const F32Scale& s, const ConstPtrTable& G, const Ptr
     PtrTable o{};
     if (out) o = *out;
     // the kernel walks s.tiles_per_mat * s.cnt tiles grid-stride
-    // MUON_F32_SCALE_WG_CAP=n lowers the cap (read at every call; for tests
-    // of the several-tiles path, which only very large inputs reach otherwise)
-    int64_t cap = kMaxF32ScaleBlocks;
-    if (const char* e = getenv("MUON_F32_SCALE_WG_CAP")) {
-        const long long v = atoll(e);
-        if (v >= 1 && v < cap) cap = v;
-    }
+    // MUON_F32_SCALE_WG_CAP=n lowers the cap (read once per process; tests of
+    // the several-tiles path, which only very large inputs reach otherwise,
+    // run in a process of their own with it set)
+    static const int64_t cap = [] {
+        const char* e = getenv("MUON_F32_SCALE_WG_CAP");
+        const long long v = e ? atoll(e) : 0;
+        return (v >= 1 && v < kMaxF32ScaleBlocks) ? static_cast<int64_t>(v) : kMaxF32ScaleBlocks;
+    }();
     const int64_t total = static_cast<int64_t>(s.tiles_per_mat) * s.cnt;
     const int64_t grid = total < cap ? total : cap;
     k_f32_scale<<<static_cast<unsigned>(grid), FT_THREADS, 0, stream>>>(s, G, o);

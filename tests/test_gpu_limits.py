@@ -63,35 +63,25 @@ def test_shortest_side_at_its_limit(muon):
         parity.assert_ns5_parity(out[np.ix_(rows[b], cols[b])], want, f"block {b}")
 
 
-# The float32 matrix cores' accumulator departs from round-to-nearest by an
-# amount that grows with the length of the sum: on 16 x K Gaussian inputs the
-# float32 iteration lands 1.9e-6, 5.1e-6, 1.8e-5, 8.9e-5 and 7.3e-4 from the
-# oracle (float64 accumulation) at K = 2^12, 2^14, 2^16, 2^18 and 2^20, where a
-# sequential round-to-nearest float32 accumulator lands 1.8e-6 .. 5.3e-5.  The
-# float32 bar (1e-4, from the workloads' K <= 6400) therefore does not carry to
-# K = 2^20; there the bar is 2e-3, and the float32 iteration must still sit at
-# least five times closer to its oracle than the bf16 iteration does (measured:
-# 7.3e-4 against 7.6e-3).
-F32_LONG_K_TOL = 2e-3
-
-
+# The float32 products sum K in blocks of 1024 values, each block's sum added
+# with one float32 rounding; tests/test_fp32_model.py pins on the CPU that
+# this keeps even K = 2^20 within a tenth of the float32 bar, so the bar is
+# the same at every K.  16 x K for K = 2^16, 2^18 and 2^20, and the transpose
+# at 2^20.
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("tall", [False, True], ids=["16x2^20", "2^20x16"])
-def test_float32_iteration_longest_side(muon, longest, tall):
-    G = longest[0]
+@pytest.mark.parametrize("K,tall", [(1 << 16, False), (1 << 18, False), (1 << 20, False), (1 << 20, True)],
+                         ids=["16x2^16", "16x2^18", "16x2^20", "2^20x16"])
+def test_float32_iteration_long_sums(muon, longest, K, tall):
+    G = np.ascontiguousarray(longest[0][:, :K])
     want = oracle.ns5(G, precision="f32")
-    bf16_dist = parity.rel_fro(longest[1], want)
+    bf16_dist = parity.rel_fro(longest[1], want) if K == muon.MAX_LONG else None
     if tall:
         G, want = np.ascontiguousarray(G.T), np.ascontiguousarray(want.T)
     print(f"float32 iteration {G.shape}", flush=True)
     out = parity.to_np(muon.newton_schulz_f32([torch.from_numpy(G).cuda()])[0])
     torch.cuda.synchronize()
-    assert np.all(np.isfinite(out))
-    r = parity.rel_fro(out, want)
-    d = np.max(np.abs(parity.svals(out) - parity.svals(want)))
-    print(f"relative Frobenius {r:.3g}, singular values {d:.3g}, bf16 iteration {bf16_dist:.3g}", flush=True)
-    assert r <= F32_LONG_K_TOL and d <= F32_LONG_K_TOL, (r, d)
-    assert r * 5 <= bf16_dist, (r, bf16_dist)
+    r = parity.assert_f32_parity(out, want, f"{G.shape}")
+    print(f"relative Frobenius {r:.3g}" + (f", bf16 iteration {bf16_dist:.3g}" if bf16_dist else ""), flush=True)
 
 
 @pytest.mark.timeout(600)
