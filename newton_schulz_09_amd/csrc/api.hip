@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -87,8 +88,9 @@ int band_rows(int tiles_m) {
 // A dispatch's grid (workgroups x 256 work-items) must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t{1} << 32) / kThreads - 1;
 // Cast workgroups per launch: beyond this each casts several tiles.
-// MUON_CAST_WG_CAP=n lowers the cap (read at every call; for tests of the
-// several-tiles path, which only very large inputs reach otherwise).
+// MUON_CAST_WG_CAP=n lowers the cap (read once per process; tests of the
+// several-tiles path, which only very large inputs reach otherwise, run in
+// a process of their own with it set).
 // 64 x 64 tiles per cast workgroup (MUON_CAST_TILES=n, for tuning sweeps):
 // one norm reduction serves them all, and each next tile is loaded while
 // the current one is converted.
@@ -102,17 +104,42 @@ int cast_tiles_per_wg() {
 }
 
 int64_t max_cast_workgroups() {
-    const char* s = getenv("MUON_CAST_WG_CAP");
-    const long long v = s ? atoll(s) : 0;
-    const int64_t cap = int64_t{1} << 20;
-    return (v >= 1 && v < cap) ? v : cap;
+    static const int64_t cap = [] {
+        const char* s = getenv("MUON_CAST_WG_CAP");
+        const long long v = s ? atoll(s) : 0;
+        const int64_t limit = int64_t{1} << 20;
+        return (v >= 1 && v < limit) ? static_cast<int64_t>(v) : limit;
+    }();
+    return cap;
+}
+
+// Compute units of the current device, queried once per device (256 on a
+// whole MI355X; fewer on a partitioned one).  Without a usable device (the
+// workspace queries run on hosts with none) the whole chip's 256.
+constexpr int kDefaultCus = 256;
+constexpr int kMaxDevices = 64;
+int device_cus() {
+    static std::atomic<int> cached[kMaxDevices];  // 0: not queried yet
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultCus;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = kDefaultCus;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
 
 // Tile of the symmetric products.  With 256 tiles (m >= 2048) a pass has
 // n256 = cnt T (T + 1) / 2 upper tiles, one workgroup per CU each, so it takes
-// ceil(n256 / 256) rounds of the 256 CUs: one 4096^2 matrix has 136 tiles, a
+// ceil(n256 / CUs) rounds of the device's CUs (256 on MI355X): one 4096^2 matrix has 136 tiles, a
 // single round that leaves almost half of them idle; two have 272, a second
 // round of 16.  192 tiles on m rounded up to 192 give more, smaller tiles
 // (253 per 4096^2 matrix), each round lasting about 0.5625 / 0.85 of a 256
@@ -138,10 +165,10 @@ void choose_sym_tile(Ns5Plan* p) {
     }
     const int m192 = static_cast<int>(round_up(p->m, 192));
     if (forced == 256 || m192 < p->mp) return;  // the 192 padding must cover mp
-    constexpr double kCus = 256.0;
+    const double cus = device_cus();
     const double t256 = p->mp / 256, t192 = m192 / 192;
-    const double rounds256 = ceil(p->cnt * t256 * (t256 + 1) / 2 / kCus);
-    const double rounds192 = ceil(p->cnt * t192 * (t192 + 1) / 2 / kCus) * 0.5625 / 0.85;
+    const double rounds256 = ceil(p->cnt * t256 * (t256 + 1) / 2 / cus);
+    const double rounds192 = ceil(p->cnt * t192 * (t192 + 1) / 2 / cus) * 0.5625 / 0.85;
     if (forced == 192 || rounds192 < 0.9 * rounds256) {
         p->sym_tile = 192;
         p->msym = m192;

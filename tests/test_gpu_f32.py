@@ -146,18 +146,21 @@ def test_passes_over_one_workspace(muon):
         check(parity.to_np(outs[k]), oracle.ns5(host[k], precision="f32"), f"pass {k}")
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cap", [1, 7])
-def test_scale_several_tiles_per_workgroup(muon, monkeypatch, cap):
+def test_scale_several_tiles_per_workgroup(muon, tmp_path, cap):
     """The float32 scale kernel walks its 32 x 32 tiles grid-stride; a tiny
-    workgroup cap makes each workgroup take many tiles (as the largest shapes
-    do), with the same results as one tile per workgroup."""
+    workgroup cap (MUON_F32_SCALE_WG_CAP, read once per process, so set in a
+    child process) makes each workgroup take many tiles (as the largest
+    shapes do), with the same results as one tile per workgroup."""
+    from . import cap_child, capped
     rng = np.random.default_rng(cap)
-    host = [rng.standard_normal(s).astype(np.float32) for s in [(70, 150), (150, 70), (33, 40)]]
-    Gs = [cuda(h) for h in host]
-    want = [parity.to_np(o) for o in muon.newton_schulz_f32(Gs)]
-    want0 = [parity.to_np(o) for o in muon.newton_schulz_f32(Gs, steps=0)]
-    monkeypatch.setenv("MUON_F32_SCALE_WG_CAP", str(cap))
-    got = [parity.to_np(o) for o in muon.newton_schulz_f32(Gs)]
-    got0 = [parity.to_np(o) for o in muon.newton_schulz_f32(Gs, steps=0)]
-    for a, b in zip(got + got0, want + want0):
+    shapes = [(70, 150), (150, 70), (33, 40)]
+    arrays = {"n": np.int64(len(shapes))}
+    for k, s in enumerate(shapes):
+        arrays[f"G{k}"] = rng.standard_normal(s).astype(np.float32)
+    want = cap_child.run("f32scale", arrays)
+    got = capped.run_capped(tmp_path, "f32scale", arrays, "MUON_F32_SCALE_WG_CAP", cap)
+    assert len(got) == len(want) == 2 * len(shapes)
+    for a, b in zip(got, want):
         assert np.array_equal(a, b)
