@@ -29,6 +29,9 @@ Workloads (shapes are rows x cols of the fp32 gradient G):
   matrix i (0..15) draws from default_rng((seed, i)).
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GPT2_124M_SHAPES = [(768, 2304), (768, 768), (768, 3072), (3072, 768)]
@@ -54,21 +57,33 @@ def _lowrank_plus_noise(rng, rows, cols, rank=16):
     return G.astype(np.float32), buf.astype(np.float32)
 
 
+def _workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def gpt_hidden_set(shapes, layers, seed, only_shape=None):
     """Gradients and momentum buffers for ``layers`` x ``shapes``.
 
     Returns a list of ``(layer, shape_index, G, buf)``, layer-major.
-    ``only_shape`` (a shape index) generates just that class.
+    ``only_shape`` (a shape index) generates just that class.  Matrices are
+    drawn on a few threads; each has its own generator, so the values do not
+    depend on the order in which they are drawn.
     """
-    out = []
-    for layer in range(layers):
-        for si, (r, c) in enumerate(shapes):
-            if only_shape is not None and si != only_shape:
-                continue
-            rng = np.random.default_rng((seed, layer, si))
-            G, buf = _lowrank_plus_noise(rng, r, c)
-            out.append((layer, si, G, buf))
-    return out
+    keys = [(layer, si) for layer in range(layers) for si in range(len(shapes))
+            if only_shape is None or si == only_shape]
+
+    def one(key):
+        layer, si = key
+        r, c = shapes[si]
+        G, buf = _lowrank_plus_noise(np.random.default_rng((seed, layer, si)), r, c)
+        return (layer, si, G, buf)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        return list(ex.map(one, keys))
 
 
 def gpt2_124m(seed=1, only_shape=None):

@@ -248,29 +248,27 @@ def test_batched_zero_steps_and_aliasing(muon):
 
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cap", [1, 7, 100])
-def test_cast_several_tiles_per_workgroup(muon, monkeypatch, cap):
+def test_cast_several_tiles_per_workgroup(muon, tmp_path, cap):
     """Very large inputs make each cast workgroup handle several 64x64 tiles of
-    one matrix; a low cap (MUON_CAST_WG_CAP) forces that path here.  X0, the
-    NS5 result and the fused step's outputs and buffers are bitwise those of
-    the one-tile path, for wide, tall, ragged and tile-aligned shapes."""
+    one matrix; a low cap (MUON_CAST_WG_CAP, read once per process, so set in
+    a child process) forces that path here.  X0, the NS5 result and the fused
+    step's outputs and buffers are bitwise those of the one-tile path, for
+    wide, tall, ragged and tile-aligned shapes."""
+    from . import cap_child, capped
     shapes = [(200, 520), (520, 200), (64, 128), (3, 5), (768, 768), (130, 65)]
     rng = np.random.default_rng(31)
-    Gs = [cuda(rng.standard_normal(s).astype(np.float32)) for s in shapes]
-    b0 = [cuda((0.1 * rng.standard_normal(s)).astype(np.float32)) for s in shapes]
-
-    def run():
-        bufs = [b.clone() for b in b0]
-        return (muon.ns5_batched(Gs, steps=0), muon.ns5_batched(Gs),
-                muon.ns5_batched(Gs, bufs=bufs), bufs)
-
-    want = run()
-    monkeypatch.setenv("MUON_CAST_WG_CAP", str(cap))
-    got = run()
-    torch.cuda.synchronize()
-    for part, (w_list, g_list) in zip(("X0", "NS5", "fused", "buffers"), zip(want, got)):
-        for k, (w, g) in enumerate(zip(w_list, g_list)):
-            assert torch.equal(w, g), f"{part} of matrix {k} {shapes[k]} differs with cap {cap}"
+    arrays = {"n": np.int64(len(shapes))}
+    for k, s in enumerate(shapes):
+        arrays[f"G{k}"] = rng.standard_normal(s).astype(np.float32)
+        arrays[f"B{k}"] = (0.1 * rng.standard_normal(s)).astype(np.float32)
+    want = cap_child.run("cast", arrays)
+    got = capped.run_capped(tmp_path, "cast", arrays, "MUON_CAST_WG_CAP", cap)
+    assert len(got) == len(want) == 4 * len(shapes)
+    for k, (w, g) in enumerate(zip(want, got)):
+        part = ("X0", "NS5", "fused", "buffers")[k // len(shapes)]
+        assert np.array_equal(w, g), f"{part} of matrix {k % len(shapes)} {shapes[k % len(shapes)]} differs with cap {cap}"
 
 
 # ---------------------------------------------------------------- fused Muon step
@@ -381,11 +379,19 @@ def _apply_reference(p, O, lr):
     return (p.astype(np.float64) - np.float64(np.float32(lr)) * O.astype(np.float64)).astype(np.float32)
 
 
+def _ulp32(x):
+    x = np.abs(np.asarray(x, dtype=np.float32))
+    return (np.nextafter(x, np.float32(np.inf)) - x).astype(np.float64)
+
+
 @pytest.mark.parametrize("steps", [5, 0])
 def test_apply_step_updates_parameters(muon, steps):
-    """muon_momentum_ns5_apply_batched: the buffers are those of the step
-    without the update, and the parameters become p - lr * O with the O that
-    step returns (one float32 rounding); O itself meets the parity bar."""
+    """muon_momentum_ns5_apply_batched against the oracle's whole step
+    (oracle.muon_step_apply): the buffers within 1 float32 ulp and the
+    parameters within lr times the NS5 parity bar plus one float32 ulp per
+    entry.  Against the step without the update, the buffers are bitwise
+    equal and the parameters are p - lr * O with that step's O (one float32
+    rounding)."""
     rng = np.random.default_rng(51)
     shapes = [(64, 128), (128, 64), (200, 520), (520, 200), (3, 5), (768, 768), (33, 17)]
     gs = [rng.standard_normal(s).astype(np.float32) for s in shapes]
@@ -398,37 +404,38 @@ def test_apply_step_updates_parameters(muon, steps):
     p2 = [cuda(p) for p in ps]
     muon.ns5_batched([cuda(g) for g in gs], p2, steps=steps, bufs=b2, mu=0.9, lr=lr)
     torch.cuda.synchronize()
+    want_b, want_p = oracle.muon_step_apply(gs, bs, ps, mu=0.9, lr=lr, steps=steps)
+    _, want_o = oracle.muon_step(gs, bs, mu=0.9, steps=steps)
     for k, s in enumerate(shapes):
         assert torch.equal(b1[k], b2[k]), f"buffers {s}"
+        assert parity.ulp_diff32(parity.to_np(b2[k]), want_b[k]).max() <= 1, f"buffers {s}"
+        got = parity.to_np(p2[k]).astype(np.float64)
+        err = np.linalg.norm(got - want_p[k])
+        tol = parity.REL_FRO_TOL if steps else 2.0 ** -8  # steps = 0: X0, within one bf16 ulp
+        bound = lr * tol * np.linalg.norm(want_o[k].astype(np.float64)) + np.linalg.norm(_ulp32(want_p[k]))
+        assert err <= bound, f"update {s}: {err:.4g} > {bound:.4g}"
         O = parity.to_np(outs[k])
-        want = _apply_reference(ps[k], O, lr)
-        d = parity.ulp_diff32(parity.to_np(p2[k]), want)
+        d = parity.ulp_diff32(parity.to_np(p2[k]), _apply_reference(ps[k], O, lr))
         assert d.max() <= 1 and np.mean(d == 0) >= 0.999, f"update {s}"
-        _, u = oracle.momentum_nesterov(gs[k], bs[k], 0.9)
         if steps:
-            parity.assert_ns5_parity(O, oracle.ns5(u, steps=steps), f"O {s}")
+            parity.assert_ns5_parity(O, want_o[k], f"O {s}")
 
 
 # ---------------------------------------------------------------- bfloat16 in, bfloat16 out
-
-# A 33x17 Gaussian matrix is the one input here on which the iteration's
-# amplification of accumulation-order differences exceeds the parity bar
-# between two exact-rounding references: the oracle's algorithm accumulated
-# in float32 instead of float64 lands 1.49e-2 (relative Frobenius) from the
-# oracle, and the GPU (float32 accumulators) lands on the former.  It is kept
-# for the I/O path; the bar is asserted on the other shapes.
-_SENSITIVE = {(33, 17)}
-
 
 @pytest.mark.parametrize("steps", [5, 0])
 def test_bf16_inputs_give_bf16_outputs(muon, steps):
     """muon_ns5_batched_bf16: the output is the last iterate in G's dtype.  It
     agrees with the float32 entry point on the same values but for rare ties
     of the norm's summation order, is no further from the oracle than that
-    path is, and meets the parity bar; odd widths take the unaligned paths."""
-    rng = np.random.default_rng(71)
-    shapes = [(64, 128), (128, 64), (200, 520), (520, 200), (3, 5), (768, 768), (33, 17), (130, 65)]
-    host = [oracle.round_bf16(rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    path is, and meets the parity bar; odd widths take the unaligned paths.
+    The bar of each small input is the stated one unless the oracle's
+    algorithm evaluated with float32 accumulation (tests/fp32_model.py) lands
+    beyond it on the CPU: then 1.25 times that distance (the 33 x 17 input,
+    where the model lands 1.49e-2 from the oracle)."""
+    from .test_fp32_model import bf16_io_inputs
+    inputs = bf16_io_inputs()
+    shapes, host = list(inputs), list(inputs.values())
     G16 = [torch.from_numpy(h).to("cuda").to(torch.bfloat16) for h in host]
     out16 = muon.ns5_batched(G16, steps=steps)
     out32 = muon.ns5_batched([cuda(h) for h in host], steps=steps)
@@ -441,8 +448,9 @@ def test_bf16_inputs_give_bf16_outputs(muon, steps):
         want = oracle.ns5(h, steps=steps)
         if steps:
             assert parity.rel_fro(got, want) <= parity.rel_fro(parity.to_np(o32), want) + 1e-3, s
-            if s not in _SENSITIVE:
-                parity.assert_ns5_parity(got, want, f"bf16 {s}")
+            bar = parity.model_bar(h) if h.size <= 20000 else (parity.REL_FRO_TOL, parity.SIGMA_TOL)
+            r = parity.assert_ns5_parity(got, want, f"bf16 {s}", bar=bar)
+            print(f"bf16 {s}: relative Frobenius {r:.3g} (bar {bar[0]:.3g})", flush=True)
         else:
             d = parity.bf16_ulp_diff(got, want)
             assert d.max() <= 1 and np.mean(d == 0) >= 0.999
