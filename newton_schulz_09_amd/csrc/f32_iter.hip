@@ -31,13 +31,14 @@ constexpr int FK = 16;         // K step
 constexpr int FLD = FT + 4;    // LDS row length (floats): k-major rows of 128 plus 4
 constexpr int FT_THREADS = 256;
 constexpr int kFKBlock = 64;   // K steps (of FK) per block of the two-level sum: 1024 K values
+constexpr int kSplitK = 4096;  // longest K summed in one level
 constexpr int64_t kMaxF32ScaleBlocks = int64_t{1} << 20;  // scale workgroups per launch
 
 // MFMA v_mfma_f32_32x32x2_f32 operand layout: lane l supplies A[l % 32][l / 32]
 // of the 32 x 2 left operand and B[l / 32][l % 32] of the 2 x 32 right one;
 // accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4,
 // column l % 32 of the 32 x 32 result.
-template <int KIND>
+template <int KIND, bool SPLIT>
 __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
     constexpr bool QT = (KIND == GEMM_SYRK);  // Q given as N x K rows (X X^T)
@@ -107,12 +108,15 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
         }
     };
 
-    // Two-level sum: the matrix cores accumulate one block of kFKBlock K
-    // steps (1024 K values) at a time into `acc`, and each block's sum is
-    // added to `tot` with one float32 rounding, block after block.  The
-    // matrix cores' accumulator drifts from a round-to-nearest sum by an
-    // amount that grows with the number of terms it carries, so capping that
-    // number keeps a long K as close to the float64 sum as a short one.
+    // SPLIT (long K): a two-level sum.  The matrix cores accumulate one block
+    // of kFKBlock K steps (1024 K values) at a time into `acc`, and each
+    // block's sum is added to `tot` with one float32 rounding, block after
+    // block.  The matrix cores' accumulator drifts from a round-to-nearest
+    // sum by an amount that grows with the number of terms it carries, so
+    // capping that number keeps a long K as close to the float64 sum as a
+    // short one.  The second set of accumulators costs registers (two waves
+    // per SIMD instead of four), so sums of up to kSplitK terms keep the one
+    // level.
     f32x16 acc[2][2], tot[2][2];
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm], bq[fn], acc[fm][fn], 0, 0, 0);
         }
         if (kt + 1 < nk) lstore(cur ^ 1);
-        if ((kt + 1) % kFKBlock == 0 || kt + 1 == nk) {  // close the block
+        if (SPLIT && ((kt + 1) % kFKBlock == 0 || kt + 1 == nk)) {  // close the block
 #pragma unroll
             for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_gemm(F32Gemm g, PtrTable out
             for (int r = 0; r < 16; ++r) {
                 const int i = i0 + wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
                 const int j = j0 + wn * 64 + fn * 32 + fr;
-                float v = tot[fm][fn][r];
+                float v = SPLIT ? tot[fm][fn][r] : acc[fm][fn][r];
                 if constexpr (KIND == GEMM_SYRK) {
                     // upper tiles hold (i, j) and its mirror; a diagonal tile
                     // writes i <= j only, so A is exactly symmetric
@@ -270,11 +274,16 @@ __global__ __launch_bounds__(FT_THREADS) void k_f32_scale(F32Scale s, ConstPtrTa
 hipError_t launch_f32_gemm(GemmKind kind, const F32Gemm& g, int blocks, const PtrTable* out, hipStream_t stream) {
     PtrTable o{};
     if (out) o = *out;
-    switch (kind) {
-        case GEMM_SYRK: k_f32_gemm<GEMM_SYRK><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
-        case GEMM_AAB: k_f32_gemm<GEMM_AAB><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
-        case GEMM_BX: k_f32_gemm<GEMM_BX><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
-        case GEMM_BX_FINAL: k_f32_gemm<GEMM_BX_FINAL><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+    const bool split = g.K > kSplitK;
+    switch (kind * 2 + (split ? 1 : 0)) {
+        case GEMM_SYRK * 2: k_f32_gemm<GEMM_SYRK, false><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_SYRK * 2 + 1: k_f32_gemm<GEMM_SYRK, true><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_AAB * 2: k_f32_gemm<GEMM_AAB, false><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_AAB * 2 + 1: k_f32_gemm<GEMM_AAB, true><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_BX * 2: k_f32_gemm<GEMM_BX, false><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_BX * 2 + 1: k_f32_gemm<GEMM_BX, true><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_BX_FINAL * 2: k_f32_gemm<GEMM_BX_FINAL, false><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
+        case GEMM_BX_FINAL * 2 + 1: k_f32_gemm<GEMM_BX_FINAL, true><<<blocks, FT_THREADS, 0, stream>>>(g, o); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -63,10 +63,10 @@ def test_shortest_side_at_its_limit(muon):
         parity.assert_ns5_parity(out[np.ix_(rows[b], cols[b])], want, f"block {b}")
 
 
-# The float32 products sum K in blocks of 1024 values, each block's sum added
-# with one float32 rounding; tests/test_fp32_model.py pins on the CPU that
-# this keeps even K = 2^20 within a tenth of the float32 bar, so the bar is
-# the same at every K.  16 x K for K = 2^16, 2^18 and 2^20, and the transpose
+# The float32 products sum a K beyond 4096 in blocks of 1024 values, each
+# block's sum added with one float32 rounding; tests/test_fp32_model.py pins
+# on the CPU that this keeps even K = 2^20 within a tenth of the float32 bar,
+# so the bar is the same at every K.  16 x K for K = 2^16, 2^18 and 2^20, and the transpose
 # at 2^20.
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("K,tall", [(1 << 16, False), (1 << 18, False), (1 << 20, False), (1 << 20, True)],
