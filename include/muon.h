@@ -12,7 +12,8 @@
  *  - Matrices are dense, row-major and contiguous (leading dimension = cols),
  *    in device memory.  The caller owns every buffer, including the
  *    workspace; the library allocates nothing and keeps no state between
- *    calls.
+ *    calls (muon_momentum_ns5_batched_static alone uses a device array the
+ *    library holds as its workspace).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is enqueued on it and the call returns without synchronising.
  *  - Arguments are validated before anything is enqueued; a validation error
@@ -307,6 +308,35 @@ int muon_ns5_batched_timed(const float* const* G, float* const* out, float* cons
                            const int64_t* rows, const int64_t* cols, int64_t count, int steps, float eps,
                            void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                            int n_event_pairs, int* recorded);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The Muon
+ * step of muon_momentum_ns5_batched, with the workspace taken from a device
+ * array the library holds instead of a caller argument: MUON_STATIC_WORKSPACE_BYTES
+ * per GPU, allocated when the library's code is loaded on that GPU and kept
+ * until the process ends.  The call itself allocates no device memory (its
+ * host-side planning uses small host containers).
+ *  g, buf, out, rows, cols, count, mu, steps, eps, stream : as
+ *         muon_momentum_ns5_batched (device pointers in host arrays; the
+ *         caller owns them).
+ * Results are bitwise those of muon_momentum_ns5_batched.  A batch whose
+ * workspace exceeds MUON_STATIC_WORKSPACE_BYTES runs in more launch groups
+ * (each fitting in it), one after another; a matrix whose own workspace
+ * exceeds it (muon_ns5_workspace_size(rows, cols, 1) > the size: a square
+ * matrix of side above 5632, or 4096 x 16384) is rejected.
+ * Every call on one GPU uses that GPU's single array: calls that overlap in
+ * time on one GPU (different streams, threads or processes' graphs replayed
+ * concurrently) race and give undefined results; order them on one stream.
+ * Errors: as muon_momentum_ns5_batched, plus MUON_ERR_UNSUPPORTED for a
+ * matrix too large for the static workspace, and MUON_ERR_HIP if no device
+ * is current or the array's address cannot be found; nothing is enqueued
+ * then.
+ */
+#define MUON_STATIC_WORKSPACE_BYTES (256u << 20)
+int muon_momentum_ns5_batched_static(const float* const* g, float* const* buf, float* const* out,
+                                     const int64_t* rows, const int64_t* cols, int64_t count, float mu, int steps,
+                                     float eps, void* stream);
 
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* muon_status_string(int status);

@@ -254,8 +254,10 @@ int64_t bx_blocks(const Ns5Plan& p) {
 }
 
 // Splits validated segments into launch groups (deterministic in the shapes,
-// so the workspace query and the call agree).
-int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups) {
+// so the workspace query and the call agree).  cap > 0 bounds every group's
+// workspace to cap bytes (a fixed workspace): chunks are cut to fit, and a
+// matrix that needs more on its own is an error.
+int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups, size_t cap = 0) {
     groups->clear();
     for (int si = 0; si < nseg; ++si) {
         const Segment& sg = segs[si];
@@ -264,9 +266,19 @@ int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups) {
             if (!make_plan(sg.rows, sg.cols, sg.count - start, &pl))
                 return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits",
                             (long long)sg.rows, (long long)sg.cols);
+            while (cap > 0 && pl.bytes > cap) {
+                if (pl.cnt == 1)
+                    return fail(MUON_ERR_UNSUPPORTED,
+                                "a %lld x %lld matrix needs %zu bytes of workspace, more than the %zu the "
+                                "library holds", (long long)sg.rows, (long long)sg.cols, pl.bytes, cap);
+                // bytes grow about linearly with the matrices of a chunk
+                int64_t fit = static_cast<int64_t>(static_cast<double>(pl.cnt) * cap / pl.bytes);
+                if (fit >= pl.cnt) fit = pl.cnt - 1;
+                make_plan(sg.rows, sg.cols, fit < 1 ? 1 : fit, &pl);
+            }
             Group* g = groups->empty() ? nullptr : &groups->back();
             if (!g || g->tile != pl.tile || g->chunks[0].plan.sym_tile != pl.sym_tile ||
-                g->mats + pl.cnt > kMaxGroup ||
+                g->mats + pl.cnt > kMaxGroup || (cap > 0 && g->bytes + pl.bytes > cap) ||
                 static_cast<int>(g->chunks.size()) == kMaxSeg || g->bx_blocks + bx_blocks(pl) > kMaxWorkgroups) {
                 groups->emplace_back();
                 g = &groups->back();
@@ -865,6 +877,35 @@ int run_f32(const float* const* G, float* const* out, const int64_t* rows, const
 }
 
 }  // namespace
+
+// The Muon step (momentum + NS5) on a workspace of fixed size ws_bytes:
+// launch groups are cut so that each fits, and a matrix that does not fit on
+// its own is an error (nothing enqueued).  `workspace` supplies the address
+// once the arguments have been validated.  Results are bitwise those of
+// muon_momentum_ns5_batched, whose matrices do not depend on their batch.
+int run_momentum_ns5_fixed_workspace(const float* const* g, float* const* buf, float* const* out,
+                                     const int64_t* rows, const int64_t* cols, int64_t count, float mu, int steps,
+                                     float eps, size_t ws_bytes, int (*workspace)(void**), hipStream_t stream) {
+    if (!buf) return fail(MUON_ERR_INVALID_ARG, "null momentum buffer array");
+    int st = check_common(steps, eps);
+    if (st) return st;
+    std::vector<Segment> segs;
+    std::vector<std::vector<const float*>> gs;
+    std::vector<std::vector<float*>> os, bs;
+    st = batched_segments(g, out, buf, rows, cols, count, true, &segs, &gs, &os, &bs);
+    if (st) return st;
+    std::vector<Group> groups;
+    st = plan_groups(segs.data(), static_cast<int>(segs.size()), &groups, ws_bytes);
+    if (st) return st;
+    void* ws = nullptr;  // only once the arguments are known to be valid
+    st = workspace(&ws);
+    if (st) return st;
+    st = check_workspace(ws, ws_bytes, groups_bytes(groups));
+    if (st) return st;
+    return run_groups(groups, kQuintic, Update{}, mu, steps, eps, static_cast<char*>(ws), stream, nullptr);
+}
+
+int fail_status(int status, const char* msg) { return fail(status, "%s", msg); }
 
 }  // namespace muon
 

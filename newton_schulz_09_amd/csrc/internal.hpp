@@ -49,6 +49,16 @@ struct Ns5Plan {
 
 bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* plan);
 
+// muon_momentum_ns5_batched on a workspace of fixed size (api.hip): the batch
+// runs in launch groups that each fit in ws_bytes; `workspace` is asked for
+// the workspace's address (returning 0 or a MUON status) once the arguments
+// have been validated.
+int run_momentum_ns5_fixed_workspace(const float* const* g, float* const* buf, float* const* out,
+                                     const int64_t* rows, const int64_t* cols, int64_t count, float mu, int steps,
+                                     float eps, size_t ws_bytes, int (*workspace)(void**), hipStream_t stream);
+// Records `msg` as the calling thread's last error and returns `status`.
+int fail_status(int status, const char* msg);
+
 enum GemmKind { GEMM_SYRK = 0, GEMM_AAB = 1, GEMM_BX = 2, GEMM_BX_FINAL = 3 };
 
 // One segment of a GEMM launch: `cnt` same-shaped matrices laid out as in

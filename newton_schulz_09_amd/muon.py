@@ -37,7 +37,10 @@ EXPORTS = ("muon_momentum_nesterov", "muon_momentum_nesterov_grouped", "muon_ns5
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
            "muon_ns5_batched_bf16", "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
            "muon_ns5_batched_timed", "muon_newton_schulz_f32_workspace_size", "muon_newton_schulz_f32_batched",
-           "muon_status_string", "muon_last_error")
+           "muon_momentum_ns5_batched_static", "muon_status_string", "muon_last_error")
+#: Bytes of the device array muon_momentum_ns5_batched_static uses as its
+#: workspace (MUON_STATIC_WORKSPACE_BYTES).
+STATIC_WORKSPACE_BYTES = 256 << 20
 
 
 class MuonError(RuntimeError):
@@ -93,6 +96,10 @@ def _load():
                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
                                                    vp, sz, vp]
     lib.muon_newton_schulz_f32_batched.restype = ctypes.c_int
+    lib.muon_momentum_ns5_batched_static.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                     pi64, pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                                     vp]
+    lib.muon_momentum_ns5_batched_static.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
@@ -354,6 +361,34 @@ def ns5_batched(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None, eve
                                           float(eps), ws.data_ptr(), nbytes, stream, ev, len(events) // 2,
                                           ctypes.byref(rec)))
         ns5_batched.last_recorded = rec.value
+    return outs
+
+
+def momentum_ns5_batched_static(gs, bufs, outs=None, mu=0.95, steps=NS5_STEPS, eps=NS5_EPS):
+    """The whole Muon step over float32 matrices of any shapes, as
+    ``ns5_batched(gs, outs, bufs=bufs, mu=mu)``, with no workspace argument:
+    the library's own device array serves (muon_momentum_ns5_batched_static;
+    for callers that cannot allocate, such as code under graph capture).
+    ``bufs`` are updated in place; returns the outputs (new tensors unless
+    given: pass ``outs`` to allocate nothing here either)."""
+    gs, bufs = list(gs), list(bufs)
+    if not gs:
+        return []
+    if len(bufs) != len(gs):
+        raise ValueError("bufs must match gs in length")
+    for i, (g, b) in enumerate(zip(gs, bufs)):
+        _require_f32_cuda(g, f"gs[{i}]")
+        _require_f32_cuda(b, f"bufs[{i}]")
+        if g.dim() != 2 or b.shape != g.shape or b.device != gs[0].device or g.device != gs[0].device:
+            raise ValueError(f"gs[{i}] and bufs[{i}] must be 2-D, of one shape, on one device")
+    outs = _outputs(gs, outs)
+    n = len(gs)
+    vp = ctypes.c_void_p
+    arr = lambda ts: (vp * n)(*[t.data_ptr() for t in ts])  # noqa: E731
+    rows = (ctypes.c_int64 * n)(*[g.shape[0] for g in gs])
+    cols = (ctypes.c_int64 * n)(*[g.shape[1] for g in gs])
+    _check(lib.muon_momentum_ns5_batched_static(arr(gs), arr(bufs), arr(outs), rows, cols, n, float(mu), int(steps),
+                                                float(eps), _stream_handle(gs[0].device)))
     return outs
 
 

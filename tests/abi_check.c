@@ -52,6 +52,10 @@ int main(void) {
     expect(muon_momentum_ns5_batched(g2, NULL, o2, rows, cols, 2, 0.95f, 5, 1e-7f, (void*)0x200000, need, NULL) ==
                MUON_ERR_INVALID_ARG,
            "null momentum buffers");
+    expect(muon_momentum_ns5_batched_static(g2, NULL, o2, rows, cols, 2, 0.95f, 5, 1e-7f, NULL) ==
+               MUON_ERR_INVALID_ARG,
+           "static-workspace step without buffers");
+    expect(MUON_STATIC_WORKSPACE_BYTES == (256u << 20), "static workspace size");
     expect(muon_momentum_ns5_apply_batched(g2, b2, o2, rows, cols, 2, 0.95f, INFINITY, 5, 1e-7f, (void*)0x200000,
                                            need, NULL) == MUON_ERR_INVALID_ARG,
            "infinite learning rate");

@@ -178,6 +178,34 @@ def test_fused_step_validation_errors_before_any_launch(muon):
     assert call(g, b, o, rows, cols, 0, 0.95, 5, 1e-7, ws, need, None) == muon.MUON_ERR_INVALID_ARG
 
 
+def test_static_workspace_validation_errors_before_any_device_call(muon):
+    """muon_momentum_ns5_batched_static validates every argument, and checks
+    that each matrix fits in the library's static workspace, before it looks
+    up that workspace on the device: these run on a host with no GPU."""
+    lib = muon.lib
+    i64 = ctypes.c_int64
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    b = (ctypes.c_void_p * 2)(0x400000, 0x400100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    rows, cols = (i64 * 2)(64, 130), (i64 * 2)(128, 65)
+    call = lib.muon_momentum_ns5_batched_static
+    assert call(g, None, o, rows, cols, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_INVALID_ARG
+    nullb = (ctypes.c_void_p * 2)(0x400000, 0)
+    assert call(g, nullb, o, rows, cols, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_INVALID_ARG
+    alias = (ctypes.c_void_p * 2)(0x400000, 0x300100)       # out[1] == buf[1]
+    assert call(g, alias, o, rows, cols, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, o, rows, cols, 0, 0.95, 5, 1e-7, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, o, rows, cols, 2, 0.95, -1, 1e-7, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, b, o, rows, cols, 2, 0.95, 5, float("inf"), None) == muon.MUON_ERR_INVALID_ARG
+    # the largest square that fits, and the next step up, which does not
+    assert muon.workspace_size(5632, 5632, 1) <= muon.STATIC_WORKSPACE_BYTES < muon.workspace_size(5648, 5648, 1)
+    big = (i64 * 2)(5648, 130)
+    assert call(g, b, o, big, big, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_UNSUPPORTED
+    assert b"the library holds" in lib.muon_last_error()
+    huge = (i64 * 2)(1 << 15, 64)                           # beyond MUON_NS5_MAX_SHORT
+    assert call(g, b, o, huge, huge, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_UNSUPPORTED
+
+
 def test_coefficient_validation_errors_before_any_launch(muon):
     lib = muon.lib
     i64 = ctypes.c_int64
