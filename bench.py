@@ -24,7 +24,19 @@ Printed (one JSON line on stdout):
   f32_iteration  the same 48 matrices through the iteration carried in float32
                  (muon_newton_schulz_f32_batched), against the float32 matrix
                  peak, and its time over the bf16 NS5 of the same matrices
+  single_64x128  one 64x128 Muon step (momentum + NS5) and its 128x64
+                 transpose, microseconds per call (launch-bound)
+  gpt2_1p5b      the GPT-2 1.5B hidden set (192 matrices, 48 layers x 1600x4800,
+                 1600x1600, 1600x6400, 6400x1600), one fused Muon step
+  extreme_aspect eight 2048x8192 and eight 8192x2048 matrices, one batched NS5
   cpu_baseline   the CPU oracle on a bounded sample of the same step
+  cpu_samples    the CPU oracle on samples of the other workloads, scaled to
+                 their whole size
+
+Every NS5 rate is given twice: on the nominal flops 5 (4 m^2 n + 2 m^3) of
+the metric, and on the symmetry-aware minimum 5 (3 m^2 n + m^3) (X X^T and
+A A are symmetric, so half of each is a mirror); the kernels compute upper
+tiles only, so the second is the closer measure of the matrix cores' work.
 """
 
 import argparse
@@ -55,6 +67,8 @@ def parse():
     p.add_argument("--skip-cpu-baseline", action="store_true")
     p.add_argument("--skip-square", action="store_true", help="skip the 4096x4096 NS5 line")
     p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
+    p.add_argument("--only", choices=["square_4096", "extreme_aspect", "gpt2_1p5b", "single_64x128"],
+                   help="time only this workload (for profiling its kernels); prints its line alone")
     p.add_argument("--svd-context", action="store_true",
                    help="only time U V^T from the ROCm library SVD (torch.linalg.svd) on the same 48 matrices and "
                         "on the 4096x4096 matrix, next to NS5: context for the claim that an SVD would be too slow "
@@ -197,18 +211,10 @@ def time_square(torch, muon, workloads, reps=10):
     G, _, _, _ = workloads.square_4096()
     g = torch.from_numpy(G).cuda()
     out = torch.empty_like(g)
-    for _ in range(3):
-        muon.ns5(g, out)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        muon.ns5(g, out)
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / reps
-    tf = muon.ns5_flops(4096, 4096) / (ms * 1e-3) / 1e12
-    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    ms = _timed(torch, lambda: muon.ns5(g, out), reps, warm=3)
+    res = {"ms": round(ms, 4)}
+    res.update(_rates(muon.ns5_flops(4096, 4096), sym_min_flops(4096, 4096), ms))
+    return res
 
 
 def time_f32_iteration(st, torch, muon, reps=3):
@@ -234,6 +240,118 @@ def time_f32_iteration(st, torch, muon, reps=3):
     tf = st.nominal_ns5_flops() / (timings["f32"] * 1e-3) / 1e12
     return {"ms": round(timings["f32"], 3), "TFLOP/s": round(tf, 2), "pct_f32_mfma_peak": round(100 * tf / PEAK_F32_TFLOPS, 2),
             "bf16_ns5_ms": round(timings["bf16"], 4), "f32_over_bf16": round(timings["f32"] / timings["bf16"], 2)}
+
+
+def sym_min_flops(rows, cols, steps=5):
+    """Symmetry-aware minimum NS5 flops, 5 (3 m^2 n + m^3): the upper half of
+    X X^T (m^2 n) and of A A (m^3), and all of B X (2 m^2 n)."""
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (3 * m * m * n + m ** 3)
+
+
+def _rates(nominal, symmin, ms):
+    tf = nominal / (ms * 1e-3) / 1e12
+    tf_min = symmin / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "TFLOP/s_symmetric_min": round(tf_min, 2),
+            "pct_mfma_peak_symmetric_min": round(100 * tf_min / PEAK_BF16_TFLOPS, 2)}
+
+
+def _timed(torch, fn, reps, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
+def time_single_64x128(torch, muon, workloads, reps=200):
+    """The 64x128 matrix and its 128x64 transpose: one Muon step each
+    (muon_momentum_ns5_batched on one matrix), microseconds per call."""
+    G, buf = workloads.single_64x128()
+    res = {}
+    for name, M, B in (("64x128", G, buf), ("128x64", G.T, buf.T)):
+        g = torch.from_numpy(M.copy()).cuda()
+        b = torch.from_numpy(B.copy()).cuda()
+        o = torch.empty_like(g)
+        ms = _timed(torch, lambda: muon.ns5_batched([g], [o], bufs=[b]), reps, warm=5)
+        res[f"us_per_call_{name}"] = round(ms * 1e3, 2)
+    g2 = [torch.from_numpy(G.copy()).cuda(), torch.from_numpy(G.T.copy()).cuda()]
+    b2 = [torch.zeros_like(x) for x in g2]
+    o2 = [torch.empty_like(x) for x in g2]
+    res["us_per_call_both_batched"] = round(_timed(torch, lambda: muon.ns5_batched(g2, o2, bufs=b2), reps, 5) * 1e3, 2)
+    return res
+
+
+def time_gpt2_1p5b(torch, muon, step, workloads, reps=5):
+    """One fused Muon step over the GPT-2 1.5B hidden set (192 matrices)."""
+    t0 = time.time()
+    items = workloads.gpt2_1p5b()
+    st = step.MuonStep([it[2].shape for it in items], device="cuda:0")
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    del items
+    torch.cuda.synchronize()
+    log(f"gpt2-1.5b inputs ready in {time.time() - t0:.1f} s")
+    ms = _timed(torch, st.fused_step, reps)
+    res = {"ms_per_step": round(ms, 3), "matrices": len(st.shapes), "nominal_ns5_flops": st.nominal_ns5_flops(),
+           "momentum_bytes": st.momentum_bytes()}
+    res.update(_rates(st.nominal_ns5_flops(), sum(sym_min_flops(r, c) for r, c in st.shapes), ms))
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_extreme_aspect(torch, muon, workloads, reps=5):
+    """Eight 2048x8192 and eight 8192x2048 matrices in one muon_ns5_batched
+    call (pure NS5, no momentum)."""
+    items = workloads.extreme_aspect()
+    Gs = [torch.from_numpy(it[0]).cuda() for it in items]
+    shapes = [tuple(g.shape) for g in Gs]
+    del items
+    outs = [torch.empty_like(g) for g in Gs]
+    ws = torch.empty(muon.batched_workspace_size(shapes), dtype=torch.uint8, device="cuda")
+    ms = _timed(torch, lambda: muon.ns5_batched(Gs, outs, workspace=ws), reps)
+    nominal = sum(muon.ns5_flops(r, c) for r, c in shapes)
+    res = {"ms": round(ms, 3), "matrices": len(shapes), "nominal_ns5_flops": nominal}
+    res.update(_rates(nominal, sum(sym_min_flops(r, c) for r, c in shapes), ms))
+    return res
+
+
+def cpu_samples(workloads):
+    """The oracle on bounded samples of the other workloads, each scaled to
+    its whole size: the 64x128 step and its transpose whole; one matrix of
+    each of the four GPT-2 1.5B shape classes (momentum + NS5), scaled by 48;
+    one 2048x8192 and one 8192x2048 matrix (NS5), scaled by 8."""
+    import oracle
+    res = {}
+    G, buf = workloads.single_64x128()
+    t0 = time.perf_counter()
+    for M, B in ((G, buf), (G.T, buf.T)):
+        _, u = oracle.momentum_nesterov(M, B, 0.95)
+        oracle.ns5(u)
+    res["single_64x128_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+    t0 = time.perf_counter()
+    for si in range(4):
+        _, _, G, buf = workloads.gpt_hidden_set(workloads.GPT2_1P5B_SHAPES, 1, 4, only_shape=si)[0]
+        _, u = oracle.momentum_nesterov(G, buf, 0.95)
+        oracle.ns5(u)
+    dt = time.perf_counter() - t0
+    res["gpt2_1p5b_s_per_step"] = round(dt * workloads.GPT2_1P5B_LAYERS, 1)
+    res["gpt2_1p5b_sample"] = f"layer 0, one matrix per shape class: {dt:.1f} s, x 48 layers"
+    t0 = time.perf_counter()
+    for it in workloads.extreme_aspect(indices=[0, 8]):
+        oracle.ns5(it[0])
+    dt = time.perf_counter() - t0
+    res["extreme_aspect_s"] = round(dt * 8, 1)
+    res["extreme_aspect_sample"] = f"matrices 0 (2048x8192) and 8 (8192x2048): {dt:.1f} s, x 8"
+    return res
 
 
 def svd_context(torch, muon, workloads):
@@ -308,6 +426,14 @@ def main():
 
     from newton_schulz_09_amd import muon, step, workloads
 
+    if args.only:
+        fn = {"square_4096": lambda: time_square(torch, muon, workloads),
+              "extreme_aspect": lambda: time_extreme_aspect(torch, muon, workloads),
+              "gpt2_1p5b": lambda: time_gpt2_1p5b(torch, muon, step, workloads),
+              "single_64x128": lambda: time_single_64x128(torch, muon, workloads)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
+
     t0 = time.time()
     items = workloads.gpt2_124m()
     st = step.MuonStep([it[2].shape for it in items], device="cuda:0")
@@ -350,6 +476,8 @@ def main():
         },
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
     }
+    symmin = sum(sym_min_flops(r, c) for r, c in st.shapes)
+    res["pct_mfma_peak_symmetric_min"] = round(100 * symmin / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
     if not args.skip_extras:
         res["roofline"] = time_dominant_kernel(st, args.steps, torch)
         log(f"dominant kernel: {res['roofline']}")
@@ -362,9 +490,19 @@ def main():
         if not args.skip_square:
             res["ns5_4096"] = time_square(torch, muon, workloads)
             log(f"ns5 4096: {res['ns5_4096']}")
+        res["single_64x128"] = time_single_64x128(torch, muon, workloads)
+        log(f"64x128: {res['single_64x128']}")
+        res["extreme_aspect"] = time_extreme_aspect(torch, muon, workloads)
+        log(f"extreme aspect: {res['extreme_aspect']}")
+        del st
+        torch.cuda.empty_cache()
+        res["gpt2_1p5b"] = time_gpt2_1p5b(torch, muon, step, workloads)
+        log(f"gpt2 1.5b: {res['gpt2_1p5b']}")
         if not args.skip_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline(items)
             log(f"cpu baseline: {res['cpu_baseline']}")
+            res["cpu_samples"] = cpu_samples(workloads)
+            log(f"cpu samples: {res['cpu_samples']}")
     print(json.dumps(res), flush=True)
 
 
