@@ -74,10 +74,10 @@ def round_f32(x):
 
 
 def momentum_nesterov(g, buf, mu=0.95):
-    """One Nesterov-momentum step on a gradient, as the Muon section uses it
-    (summary paragraph: "Nesterov momentum in the update, orthogonalise after
-    momentum").  The update formula itself did not survive in the page; the
-    reading used is plain SGD-Nesterov without dampening:
+    """One Nesterov-momentum step on a gradient.  The Muon section's summary
+    paragraph names Nesterov momentum as part of the update and places the
+    orthogonalisation after it; the update formula itself did not survive in
+    the page, so the reading used is plain SGD-Nesterov without dampening:
 
         buf <- mu * buf + g
         u   <- g + mu * buf          (with the new buf)
@@ -93,54 +93,61 @@ def momentum_nesterov(g, buf, mu=0.95):
     return buf_new, u
 
 
+def _quintic_step(X, coeffs, rnd):
+    """One step of the iteration on a short-side-first X (m <= n rows):
+
+        X  <-  p(X X^T) X  with  p(S) = a I + b S + c S^2,
+
+    which maps every singular value s of X to a s + b s^3 + c s^5 and keeps
+    the singular vectors.  Three matrices are stored, each rounded once by
+    ``rnd``: the Gram matrix S = X X^T, the polynomial part b S + c S S, and
+    the new iterate a X + (b S + c S S) X.  Sums are carried in float64."""
+    a, b, c = coeffs
+    gram = rnd(X @ X.T)
+    poly = rnd(b * gram + c * (gram @ gram))
+    return rnd(a * X + poly @ X)
+
+
 def ns5(G, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS, precision="bf16"):
-    """Quintic Newton-Schulz orthogonalisation of one 2-D matrix, following the
-    Muon section's ``zeroth_power_via_newtonschulz5`` step by step:
+    """Quintic Newton-Schulz orthogonalisation of one 2-D matrix (Muon
+    section, the printed zeroth_power_via_newtonschulz5):
 
-        X = bf16(G) / (||G||_F + eps)              rounded to bf16
-        if rows > cols: X = X^T                     (iterate on the short side)
-        repeat ``steps`` times:
-            A = X X^T                               rounded to bf16
-            B = b A + c A A                         rounded to bf16
-            X = a X + B X                           rounded to bf16
-        if rows > cols: X = X^T
-        return X in G's dtype
+      * scale: X = G / (||G||_F + eps), the norm of the float32 input taken in
+        float64 and never rounded to bf16; in bf16 the input is cast before
+        the division and the quotient rounded again (two roundings);
+      * orientation: a matrix with more rows than columns is iterated as its
+        transpose, so the Gram matrix is the smaller one, and transposed back
+        at the end;
+      * ``steps`` applications of ``_quintic_step``, whose stored matrices
+        are rounded once each to bf16;
+      * the result in float32 (G's dtype).
 
-    The Frobenius norm is taken of the float32 input in float64 and is never
-    rounded to bf16.  Returns a float32 array of G's shape.
+    Returns a float32 array of G's shape.
 
     ``precision="f32"``: the same iteration carried in float32 instead of
     bfloat16, the precision the summary paragraph contrasts with bf16 (it
     notes the iteration stays stable in bf16, unlike methods that need
     float32): there is no bf16 cast, X = G / (||G||_F + eps) is rounded once
-    to float32, and A, B and X of every step are rounded once to float32 at
-    the same points.
+    to float32, and every stored matrix of every step is rounded once to
+    float32.
     """
     if precision not in ("bf16", "f32"):
         raise ValueError("precision is 'bf16' or 'f32'")
     G = np.asarray(G)
     if G.ndim != 2:
         raise ValueError("ns5 expects a 2-D matrix")
-    a, b, c = (f32(v) for v in coeffs)
+    k = tuple(f32(v) for v in coeffs)
     eps = f32(eps)
     u = G.astype(np.float32).astype(np.float64)
-    norm = np.sqrt(np.sum(u * u))
-    if precision == "bf16":
-        rnd = round_bf16
-        X = rnd(rnd(u) / (norm + eps))
-    else:
-        rnd = round_f32
-        X = rnd(u / (norm + eps))
+    denom = np.sqrt(np.sum(u * u)) + eps
+    rnd = round_bf16 if precision == "bf16" else round_f32
+    X = rnd(rnd(u) / denom) if precision == "bf16" else rnd(u / denom)
     tall = G.shape[0] > G.shape[1]
-    if tall:
-        X = X.T
+    W = X.T if tall else X
     for _ in range(steps):
-        A = rnd(X @ X.T)
-        B = rnd(b * A + c * (A @ A))
-        X = rnd(a * X + B @ X)
-    if tall:
-        X = X.T
-    return np.ascontiguousarray(X).astype(np.float32)
+        W = _quintic_step(W, k, rnd)
+    out = W.T if tall else W
+    return np.ascontiguousarray(out).astype(np.float32)
 
 
 def ns5_grouped(Gs, steps=NS5_STEPS, eps=NS5_EPS, coeffs=NS5_COEFFS):

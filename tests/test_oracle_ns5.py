@@ -66,7 +66,11 @@ def _bf16_mat(M):
     return [[Fraction(pins.bf16_nearest_scalar(v)) for v in row] for row in M]
 
 
+_MACS = [0]   # multiply-adds performed by _matmul, for the flop-count pin
+
+
 def _matmul(P, Q):
+    _MACS[0] += len(P) * len(Q[0]) * len(Q)
     return [[sum(P[i][k] * Q[k][j] for k in range(len(Q))) for j in range(len(Q[0]))]
             for i in range(len(P))]
 
@@ -97,6 +101,23 @@ def test_tiny_ns5_bitwise_against_exact_rationals():
             X = _transpose(X)
         want = np.array([[float(v) for v in row] for row in X], dtype=np.float32)
         assert np.array_equal(ns5(G), want), shape
+
+
+def test_nominal_flops_count_the_brute_forces_multiply_adds():
+    """oracle.ns5_nominal_flops is 2 flops per multiply-add of the plain
+    products the iteration performs (X X^T, A A and B X in full, no symmetry
+    used): counted here while the exact-rational brute force runs them, for
+    wide, tall and square shapes and several step counts."""
+    for shape, steps in (((3, 5), 5), ((5, 3), 5), ((4, 4), 2), ((2, 7), 3), ((7, 2), 1)):
+        G = workloads.gaussian(shape, seed=1).astype(np.float64)
+        X = [[Fraction(float(v)) for v in row] for row in (G if shape[0] <= shape[1] else G.T)]
+        _MACS[0] = 0
+        for _ in range(steps):
+            A = _matmul(X, _transpose(X))
+            B = _matmul(A, A)
+            X = _matmul(B, X)
+        assert 2 * _MACS[0] == oracle.ns5_nominal_flops(*shape, steps=steps), shape
+    assert oracle.ns5_nominal_flops(768, 2304) == 5 * (4 * 768 ** 2 * 2304 + 2 * 768 ** 3)
 
 
 # ---------------------------------------------------------------------------
@@ -209,3 +230,16 @@ def test_unmutated_variant_passes_all_pins():
     for check in pins.ALL_NS5_CHECKS:
         ok, detail = check(lambda G, steps=5, eps=1e-7: _ns5_variant(G, steps, eps))
         assert ok, (check.__name__, detail)
+
+
+def test_grouped_is_each_matrix_alone():
+    """oracle.ns5_grouped returns, in order, each matrix's own NS5 (the
+    matrices of a group are independent), with the steps and coefficients
+    passed through."""
+    Gs = [workloads.gaussian(s, seed=k) for k, s in enumerate([(3, 5), (5, 3), (4, 4), (3, 5)])]
+    for kw in ({}, {"steps": 2}, {"steps": 3, "coeffs": (1.5, -0.5, 0.0)}):
+        got = oracle.ns5_grouped(Gs, **kw)
+        assert len(got) == len(Gs)
+        for G, o in zip(Gs, got):
+            assert np.array_equal(o, ns5(G, **kw))
+    assert not np.array_equal(oracle.ns5_grouped(Gs)[0], oracle.ns5_grouped(Gs)[3])
