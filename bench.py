@@ -29,6 +29,8 @@ Printed (one JSON line on stdout):
   gpt2_1p5b      the GPT-2 1.5B hidden set (192 matrices, 48 layers x 1600x4800,
                  1600x1600, 1600x6400, 6400x1600), one fused Muon step
   extreme_aspect eight 2048x8192 and eight 8192x2048 matrices, one batched NS5
+  polar_svd      U V^T of the 48 124M momentum outputs through an SVD on the
+                 GPU (block one-sided Jacobi), against NS5 of the same matrices
   cpu_baseline   the CPU oracle on a bounded sample of the same step
   cpu_samples    the CPU oracle on samples of the other workloads, scaled to
                  their whole size
@@ -67,7 +69,7 @@ def parse():
     p.add_argument("--skip-cpu-baseline", action="store_true")
     p.add_argument("--skip-square", action="store_true", help="skip the 4096x4096 NS5 line")
     p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
-    p.add_argument("--only", choices=["square_4096", "extreme_aspect", "gpt2_1p5b", "single_64x128"],
+    p.add_argument("--only", choices=["square_4096", "extreme_aspect", "gpt2_1p5b", "single_64x128", "polar_svd"],
                    help="time only this workload (for profiling its kernels); prints its line alone")
     p.add_argument("--svd-context", action="store_true",
                    help="only time U V^T from the ROCm library SVD (torch.linalg.svd) on the same 48 matrices and "
@@ -324,6 +326,35 @@ def time_extreme_aspect(torch, muon, workloads, reps=5):
     return res
 
 
+def time_polar_svd(st, torch, muon, reps=2):
+    """U V^T of the 48 GPT-2 124M momentum outputs through an SVD on the GPU
+    (muon_polar_svd_grouped, one call per shape class), next to NS5 of the
+    same matrices (one muon_ns5_batched call): how much slower the SVD route
+    is, the claim of the Muon section."""
+    st.momentum()   # u = g + mu buf in HBM: the matrices both routes orthogonalise
+    classes = {}
+    for k, shape in enumerate(st.shapes):
+        classes.setdefault(shape, []).append(st.us[k])
+    outs = {sh: [torch.empty_like(t) for t in v] for sh, v in classes.items()}
+    ws = torch.empty(max(muon.polar_svd_workspace_size(*sh, len(v)) for sh, v in classes.items()),
+                     dtype=torch.uint8, device=st.device)
+    svd_ms = _timed(torch, lambda: [muon.polar_svd_grouped(v, outs[sh], workspace=ws) for sh, v in classes.items()],
+                    reps, warm=1)
+    ns5_ms = _timed(torch, lambda: muon.ns5_batched(st.us, st.outs, workspace=st.workspace), 10, warm=2)
+    return {"svd_ms": round(svd_ms, 2), "ns5_ms": round(ns5_ms, 4), "svd_over_ns5": round(svd_ms / ns5_ms, 1),
+            "matrices": len(st.shapes), "method": "block one-sided Jacobi, float32 storage, float64 arithmetic, "
+                                                  "at most 16 sweeps, all matrices of a shape class per launch"}
+
+
+def _loaded_step(torch, step, workloads):
+    items = workloads.gpt2_124m()
+    st = step.MuonStep([it[2].shape for it in items], device="cuda:0")
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    return st
+
+
 def cpu_samples(workloads):
     """The oracle on bounded samples of the other workloads, each scaled to
     its whole size: the 64x128 step and its transpose whole; one matrix of
@@ -430,7 +461,8 @@ def main():
         fn = {"square_4096": lambda: time_square(torch, muon, workloads),
               "extreme_aspect": lambda: time_extreme_aspect(torch, muon, workloads),
               "gpt2_1p5b": lambda: time_gpt2_1p5b(torch, muon, step, workloads),
-              "single_64x128": lambda: time_single_64x128(torch, muon, workloads)}[args.only]
+              "single_64x128": lambda: time_single_64x128(torch, muon, workloads),
+              "polar_svd": lambda: time_polar_svd(_loaded_step(torch, step, workloads), torch, muon)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
 
@@ -487,6 +519,8 @@ def main():
         log(f"apply step: {res['apply_step']}")
         res["f32_iteration"] = time_f32_iteration(st, torch, muon)
         log(f"float32 iteration: {res['f32_iteration']}")
+        res["polar_svd"] = time_polar_svd(st, torch, muon)
+        log(f"polar svd: {res['polar_svd']}")
         if not args.skip_square:
             res["ns5_4096"] = time_square(torch, muon, workloads)
             log(f"ns5 4096: {res['ns5_4096']}")
@@ -494,6 +528,7 @@ def main():
         log(f"64x128: {res['single_64x128']}")
         res["extreme_aspect"] = time_extreme_aspect(torch, muon, workloads)
         log(f"extreme aspect: {res['extreme_aspect']}")
+
         del st
         torch.cuda.empty_cache()
         res["gpt2_1p5b"] = time_gpt2_1p5b(torch, muon, step, workloads)

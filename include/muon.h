@@ -309,6 +309,42 @@ int muon_ns5_batched_timed(const float* const* G, float* const* out, float* cons
                            void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                            int n_event_pairs, int* recorded);
 
+/* Largest min(rows, cols) of muon_polar_svd_grouped. */
+#define MUON_POLAR_MAX_SHORT 4096
+
+/*
+ * Bytes of workspace muon_polar_svd_grouped needs for `count` matrices of
+ * rows x cols (passes of MUON_NS5_MAX_GROUP reuse it); 0 for invalid sizes
+ * or a short side above MUON_POLAR_MAX_SHORT.  256-byte aligned device
+ * memory; contents on entry do not matter.
+ */
+size_t muon_polar_svd_workspace_size(int64_t rows, int64_t cols, int64_t count);
+
+/*
+ * U V^T of each G = U S V^T, computed through an SVD on the GPU: the
+ * orthogonalisation that NS5 approximates, and that the Muon section of the
+ * Synced report on Modded-NanoGPT calls too slow for the optimizer; this
+ * entry point exists to measure that claim against NS5 on the same matrices.
+ * Block one-sided Jacobi on the rows of the short-side-first W (G or G^T):
+ * float32 storage, float64 arithmetic; a sweep pairs every two blocks of 32
+ * rows once, diagonalising each pair's 64 x 64 Gram matrix by cyclic Jacobi
+ * and rotating the pair's rows, until every two rows are orthogonal to a
+ * cosine of 1e-6 or max_sweeps sweeps have run.  The result has G's shape and
+ * orientation; for a rank-deficient G (singular values below 1e-6 of the
+ * largest) it is U_r V_r^T over the nonzero singular values.
+ *  G, out : host arrays of `count` device pointers, float32 rows x cols; out[i]
+ *           may alias G[i].
+ *  max_sweeps : 1 .. 64 (12 is ample for the workloads here).
+ *  workspace, workspace_bytes : >= muon_polar_svd_workspace_size(rows, cols,
+ *           count).
+ * Errors: MUON_ERR_INVALID_ARG (null pointers, sizes < 1, count < 1,
+ * max_sweeps out of range), MUON_ERR_UNSUPPORTED (short side above
+ * MUON_POLAR_MAX_SHORT or long side above MUON_NS5_MAX_LONG),
+ * MUON_ERR_WORKSPACE.
+ */
+int muon_polar_svd_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
+                           int max_sweeps, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  The Muon

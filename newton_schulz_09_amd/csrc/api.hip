@@ -85,6 +85,15 @@ int band_rows(int tiles_m) {
     return b;
 }
 
+// U V^T through an SVD: a block pair needs no rotation once the largest
+// cosine between two of its rows is at most kSvdTol (float32 rows: a few
+// units of float32 rounding, the orthogonality float32 storage holds); rows
+// shorter than kSvdRankTol times the longest are taken as null space (the
+// rows a zero singular value leaves are float32 rounding noise, about 1e-7
+// of the longest).
+constexpr double kSvdTol = 1e-6;
+constexpr double kSvdRankTol = 1e-6;
+
 // A dispatch's grid (workgroups x 256 work-items) must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t{1} << 32) / kThreads - 1;
 // Cast workgroups per launch: beyond this each casts several tiles.
@@ -876,6 +885,88 @@ int run_f32(const float* const* G, float* const* out, const int64_t* rows, const
     return ok();
 }
 
+// ---- U V^T through an SVD on the GPU (polar_svd.hip)
+//
+// Per pass of up to kMaxGroup same-shaped matrices: [W | J] (m_pad rows of
+// ld floats each), then per matrix two unsigned counters and m_pad float64
+// row lengths.  m is padded to whole pairs of 32-row blocks (a multiple of
+// 64, at least 64), n to a multiple of 64.
+struct SvdPlan {
+    int m, n, m_pad, n_pad, ld, cnt;
+    bool tall;
+    size_t off_wj, off_state, off_len, bytes;
+};
+
+bool plan_svd(int64_t rows, int64_t cols, int64_t count, SvdPlan* p) {
+    if (rows < 1 || cols < 1 || count < 1) return false;
+    const int64_t m = rows < cols ? rows : cols;
+    const int64_t n = rows < cols ? cols : rows;
+    if (m > MUON_POLAR_MAX_SHORT || n > MUON_NS5_MAX_LONG) return false;
+    p->m = static_cast<int>(m);
+    p->n = static_cast<int>(n);
+    p->tall = rows > cols;
+    p->m_pad = static_cast<int>(round_up(m < 64 ? 64 : m, 64));
+    p->n_pad = static_cast<int>(round_up(n, 64));
+    p->ld = p->n_pad + p->m_pad;
+    p->cnt = static_cast<int>(count < kMaxGroup ? count : kMaxGroup);
+    const size_t wj = align256(static_cast<size_t>(p->cnt) * p->m_pad * p->ld * sizeof(float));
+    p->off_wj = 0;
+    p->off_state = wj;
+    p->off_len = p->off_state + align256(static_cast<size_t>(p->cnt) * 2 * sizeof(unsigned int));
+    p->bytes = p->off_len + align256(static_cast<size_t>(p->cnt) * p->m_pad * sizeof(double));
+    return true;
+}
+
+int run_polar_svd(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
+                  int max_sweeps, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Segment sg;
+    int st = grouped_segment(G, out, count, rows, cols, &sg);
+    if (st) return st;
+    if (max_sweeps < 1 || max_sweeps > 64)
+        return fail(MUON_ERR_INVALID_ARG, "max_sweeps must be in 1 .. 64 (got %d)", max_sweeps);
+    SvdPlan pl;
+    if (!plan_svd(rows, cols, count, &pl))
+        return fail(MUON_ERR_UNSUPPORTED, "shape %lld x %lld is beyond the supported limits", (long long)rows,
+                    (long long)cols);
+    st = check_workspace(ws, ws_bytes, pl.bytes);
+    if (st) return st;
+    (void)hipGetLastError();
+    char* base = static_cast<char*>(ws);
+    for (int64_t start = 0; start < count; start += pl.cnt) {
+        const int cnt = static_cast<int>(count - start < pl.cnt ? count - start : pl.cnt);
+        ConstPtrTable gt{};
+        PtrTable ot{};
+        for (int i = 0; i < cnt; ++i) {
+            gt.p[i] = G[start + i];
+            ot.p[i] = out[start + i];
+        }
+        SvdArgs a{};
+        a.wj = reinterpret_cast<float*>(base + pl.off_wj);
+        a.mat_elems = static_cast<int64_t>(pl.m_pad) * pl.ld;
+        a.ld = pl.ld;
+        a.m = pl.m;
+        a.n = pl.n;
+        a.m_pad = pl.m_pad;
+        a.n_pad = pl.n_pad;
+        a.blocks = pl.m_pad / 32;
+        a.count = cnt;
+        a.tall = pl.tall ? 1 : 0;
+        a.tol = kSvdTol;
+        a.rank_tol = kSvdRankTol;
+        a.state = reinterpret_cast<unsigned int*>(base + pl.off_state);
+        a.inv_len = reinterpret_cast<double*>(base + pl.off_len);
+        hipError_t e = launch_svd_init(a, gt, stream);
+        if (e != hipSuccess) return hip_fail(e, "SVD set-up launch");
+        for (int sw = 0; sw < max_sweeps; ++sw) {
+            e = launch_svd_sweep(a, sw == max_sweeps - 1, stream);
+            if (e != hipSuccess) return hip_fail(e, "SVD sweep launch");
+        }
+        e = launch_svd_finish(a, ot, stream);
+        if (e != hipSuccess) return hip_fail(e, "U V^T launch");
+    }
+    return ok();
+}
+
 }  // namespace
 
 // The Muon step (momentum + NS5) on a workspace of fixed size ws_bytes:
@@ -1110,6 +1201,19 @@ int muon_ns5_batched_timed(const float* const* G, float* const* out, float* cons
                                static_cast<hipStream_t>(stream), &sink);
     if (recorded) *recorded = sink.recorded;
     return st;
+}
+
+size_t muon_polar_svd_workspace_size(int64_t rows, int64_t cols, int64_t count) {
+    using namespace muon;
+    SvdPlan pl;
+    return plan_svd(rows, cols, count, &pl) ? pl.bytes : 0;
+}
+
+int muon_polar_svd_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
+                           int max_sweeps, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace muon;
+    return run_polar_svd(G, out, count, rows, cols, max_sweeps, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
 }
 
 const char* muon_status_string(int status) {

@@ -230,4 +230,24 @@ struct F32Scale {
 };
 hipError_t launch_f32_scale(const F32Scale& s, const ConstPtrTable& G, const PtrTable* out, hipStream_t stream);
 
+// U V^T through a block one-sided Jacobi SVD (polar_svd.hip), over `count`
+// same-shaped matrices.  [W | J] per matrix: m_pad rows of ld floats, W in
+// columns [0, n_pad) and the accumulated rotation J in [n_pad, ld).
+struct SvdArgs {
+    float* wj;
+    int64_t mat_elems;   // floats per matrix (m_pad * ld)
+    int ld;              // n_pad + m_pad
+    int m, n, m_pad, n_pad;
+    int blocks;          // row blocks of 32: m_pad / 32 (even)
+    int count;
+    int tall;            // G is tall: W = G^T, Q written back transposed
+    double tol;          // largest cosine between two rows that needs no rotation
+    double rank_tol;     // rows shorter than this times the longest are null space
+    unsigned int* state; // per matrix: rotations in the current sweep, converged flag
+    double* inv_len;     // per matrix: m_pad row lengths, then their inverses
+};
+hipError_t launch_svd_init(const SvdArgs& a, const ConstPtrTable& G, hipStream_t stream);
+hipError_t launch_svd_sweep(const SvdArgs& a, bool last, hipStream_t stream);
+hipError_t launch_svd_finish(const SvdArgs& a, const PtrTable& out, hipStream_t stream);
+
 }  // namespace muon

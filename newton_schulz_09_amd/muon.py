@@ -37,7 +37,10 @@ EXPORTS = ("muon_momentum_nesterov", "muon_momentum_nesterov_grouped", "muon_ns5
            "muon_ns5_batched_workspace_size", "muon_ns5_batched", "muon_newton_schulz_batched",
            "muon_ns5_batched_bf16", "muon_momentum_ns5_batched", "muon_momentum_ns5_apply_batched",
            "muon_ns5_batched_timed", "muon_newton_schulz_f32_workspace_size", "muon_newton_schulz_f32_batched",
-           "muon_momentum_ns5_batched_static", "muon_status_string", "muon_last_error")
+           "muon_momentum_ns5_batched_static", "muon_polar_svd_workspace_size", "muon_polar_svd_grouped",
+           "muon_status_string", "muon_last_error")
+#: Largest short side of polar_svd_grouped (MUON_POLAR_MAX_SHORT).
+POLAR_MAX_SHORT = 4096
 #: Bytes of the device array muon_momentum_ns5_batched_static uses as its
 #: workspace (MUON_STATIC_WORKSPACE_BYTES).
 STATIC_WORKSPACE_BYTES = 256 << 20
@@ -100,6 +103,11 @@ def _load():
                                                      pi64, pi64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_float,
                                                      vp]
     lib.muon_momentum_ns5_batched_static.restype = ctypes.c_int
+    lib.muon_polar_svd_workspace_size.argtypes = [i64, i64, i64]
+    lib.muon_polar_svd_workspace_size.restype = sz
+    lib.muon_polar_svd_grouped.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int, vp,
+                                           sz, vp]
+    lib.muon_polar_svd_grouped.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
@@ -389,6 +397,38 @@ def momentum_ns5_batched_static(gs, bufs, outs=None, mu=0.95, steps=NS5_STEPS, e
     cols = (ctypes.c_int64 * n)(*[g.shape[1] for g in gs])
     _check(lib.muon_momentum_ns5_batched_static(arr(gs), arr(bufs), arr(outs), rows, cols, n, float(mu), int(steps),
                                                 float(eps), _stream_handle(gs[0].device)))
+    return outs
+
+
+def polar_svd_workspace_size(rows, cols, count=1):
+    return int(lib.muon_polar_svd_workspace_size(rows, cols, count))
+
+
+def polar_svd_grouped(Gs, outs=None, max_sweeps=16, workspace=None):
+    """U V^T of each same-shaped float32 matrix through an SVD on the GPU
+    (muon_polar_svd_grouped: block one-sided Jacobi), the orthogonalisation
+    NS5 approximates.  Returns the list of outputs (new tensors unless
+    given)."""
+    Gs = list(Gs)
+    if not Gs:
+        return []
+    for i, G in enumerate(Gs):
+        _require_f32_cuda(G, f"Gs[{i}]")
+    shape, device = Gs[0].shape, Gs[0].device
+    if len(shape) != 2 or any(G.shape != shape or G.device != device for G in Gs):
+        raise ValueError("all matrices must be 2-D with the same shape and device")
+    outs = _outputs(Gs, outs)
+    rows, cols = shape
+    count = len(Gs)
+    need = polar_svd_workspace_size(rows, cols, count)
+    if need == 0:
+        raise MuonError(MUON_ERR_UNSUPPORTED, f"shape {rows}x{cols} is not supported")
+    stream = _stream_handle(device)
+    ws = workspace if workspace is not None else _workspace(device, stream, need)
+    g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
+    o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    _check(lib.muon_polar_svd_grouped(g_ptrs, o_ptrs, count, rows, cols, int(max_sweeps), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), stream))
     return outs
 
 

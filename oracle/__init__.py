@@ -9,6 +9,6 @@ Every function is pinned by ``tests/test_oracle_*.py`` against facts fixed by
 the page and by mathematics (closed forms, invariants, exact brute force).
 """
 from .muon_oracle import (NS5_COEFFS, NS5_EPS, NS5_STEPS, apply_update, f32, momentum_nesterov,  # noqa: F401
-                          muon_step, muon_step_apply, ns5, ns5_grouped, ns5_nominal_flops, round_bf16,
-                          round_f32)
+                          muon_step, muon_step_apply, ns5, ns5_grouped, ns5_nominal_flops, polar_factor,
+                          round_bf16, round_f32)
 from .jacobi_svd import jacobi_svd  # noqa: F401

@@ -191,6 +191,24 @@ def muon_step_apply(gs, bufs, ps, mu=0.95, lr=0.02, steps=NS5_STEPS, eps=NS5_EPS
     return new_bufs, [apply_update(p, O, lr) for p, O in zip(ps, outs)]
 
 
+def polar_factor(G, rank_tol=1e-6):
+    """U V^T of G = U S V^T: the orthogonalisation the Muon section says NS5
+    approximates (and calls too slow to compute through an SVD).  Written as
+    its definition: the thin SVD of G in float64 (LAPACK through numpy, the
+    library primitive here), keeping the singular values above ``rank_tol``
+    times the largest; for a rank-deficient G the factor on the null space is
+    not unique, and U_r V_r^T over the kept ones is the unique part.  G = 0
+    gives 0.  Returns float32 of G's shape."""
+    A = np.asarray(G, dtype=np.float32).astype(np.float64)
+    if A.ndim != 2:
+        raise ValueError("polar_factor expects a 2-D matrix")
+    U, s, Vt = np.linalg.svd(A, full_matrices=False)
+    if s.size == 0 or s[0] == 0.0:
+        return np.zeros(A.shape, dtype=np.float32)
+    keep = s > rank_tol * s[0]
+    return (U[:, keep] @ Vt[keep]).astype(np.float32)
+
+
 def ns5_nominal_flops(rows, cols, steps=NS5_STEPS):
     """Nominal NS5 flop count, 2 flops per multiply-add: per step the products
     X X^T (2 m^2 n), A A (2 m^3) and B X (2 m^2 n), with m <= n."""

@@ -193,6 +193,19 @@ int main(int argc, char** argv) {
                   "grouped momentum");
         expect_ok(muon_momentum_nesterov(g[0], buf[0], u[0], int64_t{1} << 33, 0.95f, nullptr), "momentum 2^33");
     }
+    {
+        // U V^T through the GPU SVD, same-shaped groups (more than one pass
+        // for 130 matrices)
+        const int64_t shapes[][2] = {{3, 5}, {768, 3072}, {3072, 768}, {4096, 4096}, {16, 1 << 20}};
+        for (const auto& sh : shapes) {
+            Batch b;
+            b.add(sh[0], sh[1], sh[0] == 3 ? 130 : 2);
+            const size_t need = muon_polar_svd_workspace_size(sh[0], sh[1], b.n());
+            void* ws = set_ws(need);
+            expect_ok(muon_polar_svd_grouped(b.g.data(), b.out.data(), b.n(), sh[0], sh[1], 12, ws, need, nullptr),
+                      "polar SVD");
+        }
+    }
     if (failures) return 1;
     printf("host check ok: %ld launches\n", hostcheck::launches);
     return 0;

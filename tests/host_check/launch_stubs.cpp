@@ -201,4 +201,34 @@ hipError_t launch_f32_scale(const F32Scale& s, const ConstPtrTable& G, const Ptr
     return hipSuccess;
 }
 
+hipError_t launch_svd_init(const SvdArgs& a, const ConstPtrTable& G, hipStream_t) {
+    if (a.count < 1 || a.count > kMaxGroup) die("SVD count", a.count, 0);
+    for (int i = 0; i < a.count; ++i)
+        if (!G.p[i]) die("SVD null input", i, 0);
+    if (a.m_pad % 64 || a.n_pad % 64 || a.ld != a.m_pad + a.n_pad || a.blocks * 32 != a.m_pad)
+        die("SVD layout", a.m_pad, a.n_pad);
+    if (a.m > a.m_pad || a.n > a.n_pad || a.mat_elems != static_cast<long long>(a.m_pad) * a.ld)
+        die("SVD padding", a.m, a.n);
+    region(a.wj, a.mat_elems, a.count, a.m_pad, a.ld, a.ld, 4, "SVD [W | J]");
+    in_ws(a.state, a.count * 8ll, "SVD state");
+    in_ws(a.inv_len, static_cast<long long>(a.count) * a.m_pad * 8, "SVD row lengths");
+    ++hostcheck::launches;
+    return hipSuccess;
+}
+
+hipError_t launch_svd_sweep(const SvdArgs& a, bool, hipStream_t) {
+    region(a.wj, a.mat_elems, a.count, a.m_pad, a.ld, a.ld, 4, "SVD [W | J]");
+    if (a.blocks < 2 || a.blocks % 2) die("SVD blocks", a.blocks, 0);
+    ++hostcheck::launches;
+    return hipSuccess;
+}
+
+hipError_t launch_svd_finish(const SvdArgs& a, const PtrTable& out, hipStream_t) {
+    for (int i = 0; i < a.count; ++i)
+        if (!out.p[i]) die("SVD null output", i, 0);
+    in_ws(a.inv_len, static_cast<long long>(a.count) * a.m_pad * 8, "SVD row lengths");
+    ++hostcheck::launches;
+    return hipSuccess;
+}
+
 }  // namespace muon

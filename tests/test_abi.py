@@ -206,6 +206,24 @@ def test_static_workspace_validation_errors_before_any_device_call(muon):
     assert call(g, b, o, huge, huge, 2, 0.95, 5, 1e-7, None) == muon.MUON_ERR_UNSUPPORTED
 
 
+def test_polar_svd_validation_errors_before_any_launch(muon):
+    lib = muon.lib
+    ws = ctypes.c_void_p(0x200000)
+    g = (ctypes.c_void_p * 2)(0x100000, 0x100100)
+    o = (ctypes.c_void_p * 2)(0x300000, 0x300100)
+    need = lib.muon_polar_svd_workspace_size(64, 128, 2)
+    assert need > 0 and lib.muon_polar_svd_workspace_size(64, 128, 200) == lib.muon_polar_svd_workspace_size(64, 128, 128)
+    assert lib.muon_polar_svd_workspace_size(4097, 5000, 1) == 0          # beyond MUON_POLAR_MAX_SHORT
+    assert lib.muon_polar_svd_workspace_size(0, 5, 1) == 0
+    call = lib.muon_polar_svd_grouped
+    assert call(None, o, 2, 64, 128, 12, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, 0, 64, 128, 12, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, 2, 64, 128, 0, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, 2, 64, 128, 65, ws, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert call(g, o, 2, 5000, 5000, 12, ws, 1 << 40, None) == muon.MUON_ERR_UNSUPPORTED
+    assert call(g, o, 2, 64, 128, 12, ws, need - 256, None) == muon.MUON_ERR_WORKSPACE
+
+
 def test_coefficient_validation_errors_before_any_launch(muon):
     lib = muon.lib
     i64 = ctypes.c_int64
