@@ -71,10 +71,6 @@ def parse():
     p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
     p.add_argument("--only", choices=["square_4096", "extreme_aspect", "gpt2_1p5b", "single_64x128", "polar_svd"],
                    help="time only this workload (for profiling its kernels); prints its line alone")
-    p.add_argument("--svd-context", action="store_true",
-                   help="only time U V^T from the ROCm library SVD (torch.linalg.svd) on the same 48 matrices and "
-                        "on the 4096x4096 matrix, next to NS5: context for the claim that an SVD would be too slow "
-                        "(a library measurement, not part of the hot path)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device-to-device copy of COPY_BYTES bytes (10 times), the reference "
                         "kernel whose FETCH_SIZE / WRITE_SIZE readings scale the traffic counters")
@@ -385,39 +381,6 @@ def cpu_samples(workloads):
     return res
 
 
-def svd_context(torch, muon, workloads):
-    """U V^T via the library SVD, grouped by shape, against NS5 of the same
-    matrices (both on inputs already in HBM, one untimed call each first)."""
-    items = workloads.gpt2_124m()
-    groups = {}
-    for _, _, G, _ in items:
-        groups.setdefault(G.shape, []).append(torch.from_numpy(G))
-    batches = [torch.stack(v).cuda() for v in groups.values()]
-    Gs = [torch.from_numpy(it[2]).cuda() for it in items]
-    sq = torch.from_numpy(workloads.square_4096()[0]).cuda()
-
-    def polar(b):
-        U, _, Vh = torch.linalg.svd(b, full_matrices=False)
-        return U @ Vh
-
-    def timed(fn, reps=3):
-        fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / reps * 1e3
-
-    res = {"svd_124m_ms": round(timed(lambda: [polar(b) for b in batches]), 2),
-           "ns5_124m_ms": round(timed(lambda: muon.ns5_batched(Gs)), 3),
-           "svd_4096_ms": round(timed(lambda: polar(sq), reps=1), 2),
-           "ns5_4096_ms": round(timed(lambda: muon.ns5(sq)), 3)}
-    res["svd_over_ns5_124m"] = round(res["svd_124m_ms"] / res["ns5_124m_ms"], 1)
-    res["svd_over_ns5_4096"] = round(res["svd_4096_ms"] / res["ns5_4096_ms"], 1)
-    return res
-
-
 def cpu_baseline(items):
     """The oracle, as it stands, on the whole step (all 48 matrices: momentum
     then NS5), timed on this host's cores."""
@@ -449,10 +412,6 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(torch)
-        return
-    if args.svd_context:
-        from newton_schulz_09_amd import muon, workloads
-        print(json.dumps({"svd_context": svd_context(torch, muon, workloads)}), flush=True)
         return
 
     from newton_schulz_09_amd import muon, step, workloads

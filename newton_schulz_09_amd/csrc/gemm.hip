@@ -257,6 +257,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
             }
         }
     }
+    // the Q operand's row stride, read once: inside the K loop a reload from
+    // the kernel arguments would wait on the scalar memory counter, which LDS
+    // reads share
+    const int64_t ldq = __builtin_amdgcn_readfirstlane(args.ldq);
     // load L (< IP: P rows, else Q rows) of K step kt into LDS stage `stage`
     auto issue_one = [&](int L, int kt, int stage) {
         bf16_t* sP = lds + stage * STAGE;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
             __builtin_amdgcn_global_load_lds((global_cptr)(gp[L] + k0),
                                              (lds_ptr)(sP + (wave * IP + L) * RPI * BK), 16, 0, 0);
         else if constexpr (NN)
-            __builtin_amdgcn_global_load_lds((global_cptr)(gq[L - IP] + static_cast<int64_t>(k0) * args.ldq),
+            __builtin_amdgcn_global_load_lds((global_cptr)(gq[L - IP] + static_cast<int64_t>(k0) * ldq),
                                              (lds_ptr)(sP + BM * BK + (wave * IQ + L - IP) * RPIQ * BN), 16, 0,
                                              0);
         else

@@ -174,7 +174,8 @@ def test_square_4096(mods):
     muon, _ = mods
     G, U, s, V = workloads.square_4096()
     out = parity.to_np(muon.ns5(torch.from_numpy(G).cuda()))
-    parity.assert_ns5_parity(out, oracle.ns5(G), "4096x4096")
+    r = parity.assert_ns5_parity(out, oracle.ns5(G), "4096x4096")
+    print(f"4096x4096: relative Frobenius {r:.3g}", flush=True)
     # U^T O V is diagonal with p^5(s_i / ||G||_F) in exact arithmetic
     pred = p5(s / (np.linalg.norm(G.astype(np.float64)) + 1e-7))
     d = np.diag(U.T @ out.astype(np.float64) @ V)
