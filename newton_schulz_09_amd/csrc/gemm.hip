@@ -313,13 +313,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-    // The epilogue's second operand (AAB: A[j][i] = A[i][j]; BX: old X[i][j])
-    // is the K slice [i0, i0 + BM) of the Q operand, which passes through LDS
-    // during the K loop: for wave sub-tiles up to 64 x 64 each wave copies
-    // its values out of the stage of the matching K step, so they are never
-    // read from memory again (larger sub-tiles' copies would not fit in
-    // registers).  K steps past kpad hold only padding, whose values are zero.
+    // The second operand of the fused update (AAB: A[j][i] = A[i][j]; BX:
+    // old X[i][j]) is the K slice [i0, i0 + BM) of the Q operand, which passes
+    // through LDS during the K loop, so it is never read from memory again.
+    // a X + B X adds a X[i][j] to the accumulator inside the K loop, as soon
+    // as the K values below 64 (floor(i / 64) + 1) are summed: the same point
+    // under every tile shape and K step, so a matrix's result does not depend
+    // on its batch.  Wave sub-tiles of up to 4 fragments copy the values out
+    // of the stage of the K step that holds them (with BK = 32 that is one
+    // step before the sum reaches the point, for rows in the first half of a
+    // 64 block); larger ones (BK = 64 only) read and add them in that step.
+    // b A + c A A scales the whole sum by c, so its operand is added in the
+    // epilogue: copied out the same way for sub-tiles up to 64 x 64, staged
+    // through LDS after the loop for larger ones (their copies would not fit
+    // in registers).  K steps past kpad hold only padding, whose values are
+    // zero.
     constexpr bool CAPTURE_E = (NN || KIND == GEMM_AAB) && FM * FN <= 4;
+    constexpr bool APPLY_NOW = NN && !CAPTURE_E;
+    static_assert(!APPLY_NOW || BK == 64, "sub-tiles of more than 4 fragments add a X on BK = 64 only");
     u32x2 ev[CAPTURE_E ? FM : 1][CAPTURE_E ? FN : 1][4];
     if constexpr (CAPTURE_E) {
 #pragma unroll
@@ -330,27 +341,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 for (int g4 = 0; g4 < 4; ++g4) ev[fm][fn][g4] = u32x2{0u, 0u};
     }
 
-    // The epilogue's second operand for sub-tiles too large to capture: the
-    // BM x BN tile of E at (i0, j0), row-major (old X; for b A + c A A the
-    // symmetric A in place of its transpose), is brought into LDS stages the
-    // K loop no longer needs, with 16-byte global->LDS loads: rows [0, EH)
-    // during the last K step, into the stage that step would otherwise refill
-    // with a redundant copy, and rows [EH, BM) after the loop into the stage
-    // it read.  Each lane then reads its runs of 4 (NN: 8-byte row pieces;
-    // otherwise transposing reads of 4 rows of one column).
-    // (Pipelines whose stages cannot hold half the tile, and wave sub-tiles
-    // of more than 8 fragments, whose registers are full, load it whole after
-    // the loop, from the base of the LDS.)
-    constexpr bool STAGE_E = (NN || KIND == GEMM_AAB) && !CAPTURE_E;
+    // b A + c A A's operand for sub-tiles too large to capture: the BM x BN
+    // tile of A at (i0, j0), row-major (A is symmetric, so it stands in for
+    // its transpose), is loaded after the K loop from the base of the LDS with
+    // 16-byte global->LDS loads, in two halves of EH rows; each lane then
+    // reads its runs of 4 rows of one column with transposing reads.
+    constexpr bool STAGE_E = KIND == GEMM_AAB && !CAPTURE_E;
     constexpr int CPRE = BN / 8, RPIE = 64 / CPRE, EH = BM / 2;
-    constexpr bool E_SPLIT = STAGE_E && EH * BN <= STAGE && FM * FN <= 8;
     constexpr int NEH = EH / (RPIE > 0 ? RPIE : 1) / NW;  // loads per wave per half
     static_assert(!STAGE_E || (RPIE >= 1 && NEH >= 1 && NEH * RPIE * NW == EH),
                   "E tile shape not supported by the loader");
-    // chunk permutation of the staged rows: NN lanes read 32 consecutive rows
-    // at one column (keyed on the whole row); the transposing reads of the
-    // symmetric product read runs of 4 rows (the Q-tile permutation)
-    auto swe = [](int row) { return NN ? (row & (CPRE - 1)) : swq<CPRE>(row); };
+    // chunk permutation of the staged rows: the transposing reads read runs
+    // of 4 rows (the Q-tile permutation)
+    auto swe = [](int row) { return swq<CPRE>(row); };
     const bf16_t* Et = args.E + static_cast<int64_t>(mat) * args.e_mat + static_cast<int64_t>(i0) * args.lde + j0;
     // load i of half h of this wave's share of the E tile to `dst` (the
     // half's first row)
@@ -445,22 +448,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                     }
                 }
                 const int g = kk * NMF + q;
+                // (with two stages, the last step's loads would only refill a
+                // stage no later step reads, and are skipped)
+                if (STAGES > 2 || kt + 1 < nk) {
 #pragma unroll
-                for (int L = 0; L < NLOAD; ++L) {
-                    if ((L * LWIN) / NLOAD == g) {
-                        if (E_SPLIT && kt == nk - 1) {  // the first half of E instead of a redundant reload
-                            if (L < NEH) issue_e(L, 0, lds + sl * STAGE);
-                        } else {
-                            issue_one(L, kl, sl);
-                        }
-                    }
+                    for (int L = 0; L < NLOAD; ++L)
+                        if ((L * LWIN) / NLOAD == g) issue_one(L, kl, sl);
                 }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (E_SPLIT && NEH > NLOAD) {
-            if (kt == nk - 1)
-                for (int i = NLOAD; i < NEH; ++i) issue_e(i, 0, lds + sl * STAGE);
+        // a X[i][j] for the rows whose 64 block of K ends with this step
+        auto add_ax = [&](int fm, int fn, int g4, u32x2 e4) {
+            const float e0 = bf16_to_f32(static_cast<bf16_t>(e4.x & 0xffffu));
+            const float e1 = bf16_to_f32(static_cast<bf16_t>(e4.x >> 16));
+            const float e2 = bf16_to_f32(static_cast<bf16_t>(e4.y & 0xffffu));
+            const float e3 = bf16_to_f32(static_cast<bf16_t>(e4.y >> 16));
+            acc[fm][fn][4 * g4 + 0] = fmaf(args.alpha, e0, acc[fm][fn][4 * g4 + 0]);
+            acc[fm][fn][4 * g4 + 1] = fmaf(args.alpha, e1, acc[fm][fn][4 * g4 + 1]);
+            acc[fm][fn][4 * g4 + 2] = fmaf(args.alpha, e2, acc[fm][fn][4 * g4 + 2]);
+            acc[fm][fn][4 * g4 + 3] = fmaf(args.alpha, e3, acc[fm][fn][4 * g4 + 3]);
+        };
+        if constexpr (APPLY_NOW) {
+            const bf16_t* sQs = lds + (kt % STAGES) * STAGE + BM * BK;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int ik = i0 + wm * WTM + fm * 32;  // first row of this fragment row block
+                if (kt == ik / BK) {
+                    const int krow = ik - kt * BK + (lane & 31);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        u32x2 e4[4];
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int col = wn * WTN + fn * 32 + 8 * g4 + 4 * (lane >> 5);
+                            e4[g4] = lds_read8(sQs + krow * BN + (((col >> 3) ^ swq<CPRQ>(krow)) << 3) + (col & 7));
+                        }
+                        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e4[0]), "+v"(e4[1]), "+v"(e4[2]), "+v"(e4[3]));
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) add_ax(fm, fn, g4, e4[g4]);
+                    }
+                }
+            }
         }
         if constexpr (CAPTURE_E) {
             const bf16_t* sQs = lds + (kt % STAGES) * STAGE + BM * BK;
@@ -493,27 +522,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                     }
                 }
             }
+            if constexpr (NN) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int ik = i0 + wm * WTM + fm * 32;
+                    if (kt == (ik / 64 + 1) * (64 / BK) - 1) {
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                            for (int g4 = 0; g4 < 4; ++g4) {
+                                lgkm_wait_tie(ev[fm][fn][g4]);  // captured by asm reads
+                                add_ax(fm, fn, g4, ev[fm][fn][g4]);
+                            }
+                        }
+                    }
+                }
+            }
         }
     }
-    // drain the loads of the clamped tail steps before the epilogue (with a
-    // split E tile those are its first half, waited for below)
-    if constexpr (!E_SPLIT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // drain the loads of the clamped tail steps before the epilogue
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if constexpr (STAGE_E) {
-        // the second half of the epilogue operand, into the stage the last K
-        // step read (the first half was loaded during that step); or the
-        // whole tile from the LDS base
-        // every wave is done reading the stages (its own LDS reads are
-        // complete; loads still in flight write only the other stage)
+        // the epilogue operand's tile, from the LDS base, once every wave is
+        // done reading the stages
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
         for (int i = 0; i < NEH; ++i) {
-            if constexpr (E_SPLIT) {
-                issue_e(i, 1, lds + ((nk - 1) % STAGES) * STAGE);
-            } else {
-                issue_e(i, 0, lds);
-                issue_e(i, 1, lds + EH * BN);
-            }
+            issue_e(i, 0, lds);
+            issue_e(i, 1, lds + EH * BN);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -532,35 +569,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
     const int i0w = i0 + wm * WTM, j0w = j0 + wn * WTN;  // this wave's sub-tile origin
     // 4 bf16: rows ib..ib+3 of column j (NN: columns of row i)
     u32x2 hv[FM][FN][4];
-    constexpr bool HAS_E = KIND == GEMM_AAB || KIND == GEMM_BX || KIND == GEMM_BX_FINAL;
+    // (a X + B X added its a X inside the K loop)
+    constexpr bool HAS_E = KIND == GEMM_AAB;
     static_assert(!HAS_E || CAPTURE_E || STAGE_E, "the epilogue operand is captured or staged");
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             u32x2 es[4];
-            // row r of the staged E tile (half r / EH)
-            auto erow = [&](int r) -> const bf16_t* {
-                if constexpr (!E_SPLIT) return lds + r * BN;
-                // the stage the last K step refilled, and the one it read
-                const int st = r < EH ? (nk + STAGES - 2) % STAGES : (nk - 1) % STAGES;
-                return lds + st * STAGE + (r < EH ? r : r - EH) * BN;
-            };
-            if constexpr (STAGE_E && NN) {
-                // row wm*WTM + fm*32 + (l % 32) of the staged tile, columns
-                // 8 g4 + 4 (l / 32) .. +3 of the fragment
-                const int er = wm * WTM + fm * 32 + (lane & 31);
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ec = wn * WTN + fn * 32 + 8 * g4 + 4 * (lane >> 5);
-                    es[g4] = *reinterpret_cast<const u32x2*>(erow(er) + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
-                }
-            } else if constexpr (STAGE_E) {
+            if constexpr (STAGE_E) {
+                // rows of the staged tile: runs of 4 rows of one column
                 const int ec = wn * WTN + fn * 32 + tq_col;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int er = wm * WTM + fm * 32 + 8 * g4 + 4 * (tq_g >> 1) + (tq_r >> 2);
-                    es[g4] = lds_read_tr4(erow(er) + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
+                    es[g4] = lds_read_tr4(lds + er * BN + (((ec >> 3) ^ swe(er)) << 3) + (ec & 7));
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(es[0]), "+v"(es[1]), "+v"(es[2]), "+v"(es[3]));
             }
@@ -569,30 +592,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm_nt(GemmLaunch launch
                 float v0 = acc[fm][fn][4 * g4 + 0], v1 = acc[fm][fn][4 * g4 + 1];
                 float v2 = acc[fm][fn][4 * g4 + 2], v3 = acc[fm][fn][4 * g4 + 3];
                 if constexpr (HAS_E) {
-                    // AAB: A[i..i+3][j] = A[j][i..i+3] (symmetric); BX: old
-                    // X[i][j..j+3].  Either way the run of 4 this lane owns.
-                    u32x2 e4;
-                    if constexpr (CAPTURE_E) {
-                        if constexpr (NN) lgkm_wait_tie(ev[fm][fn][g4]);  // captured by asm reads
-                        e4 = ev[fm][fn][g4];
-                    } else {
-                        e4 = es[g4];
-                    }
+                    // b A + c (A A): A[i..i+3][j] = A[j][i..i+3] (symmetric),
+                    // the run of 4 this lane owns
+                    const u32x2 e4 = CAPTURE_E ? ev[fm][fn][g4] : es[g4];
                     const float e0 = bf16_to_f32(static_cast<bf16_t>(e4.x & 0xffffu));
                     const float e1 = bf16_to_f32(static_cast<bf16_t>(e4.x >> 16));
                     const float e2 = bf16_to_f32(static_cast<bf16_t>(e4.y & 0xffffu));
                     const float e3 = bf16_to_f32(static_cast<bf16_t>(e4.y >> 16));
-                    if constexpr (KIND == GEMM_AAB) {  // b A + c (A A)
-                        v0 = fmaf(args.beta, v0, args.alpha * e0);
-                        v1 = fmaf(args.beta, v1, args.alpha * e1);
-                        v2 = fmaf(args.beta, v2, args.alpha * e2);
-                        v3 = fmaf(args.beta, v3, args.alpha * e3);
-                    } else {  // a X + (B X)
-                        v0 = fmaf(args.alpha, e0, v0);
-                        v1 = fmaf(args.alpha, e1, v1);
-                        v2 = fmaf(args.alpha, e2, v2);
-                        v3 = fmaf(args.alpha, e3, v3);
-                    }
+                    v0 = fmaf(args.beta, v0, args.alpha * e0);
+                    v1 = fmaf(args.beta, v1, args.alpha * e1);
+                    v2 = fmaf(args.beta, v2, args.alpha * e2);
+                    v3 = fmaf(args.beta, v3, args.alpha * e3);
                 }
                 hv[fm][fn][g4].x = f32x2_to_bf16x2(v0, v1);
                 hv[fm][fn][g4].y = f32x2_to_bf16x2(v2, v3);
@@ -873,17 +883,22 @@ hipError_t launch_t(GemmKind kind, const GemmLaunch& L, int blocks, const PtrTab
             default: break;
         }
     }
-    switch (kind) {
-        case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX><<<grid, NT, 0, stream>>>(L, o); break;
-        case GEMM_BX_FINAL:
-            k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX_FINAL><<<grid, NT, 0, stream>>>(L, o);
-            break;
-        default: return hipErrorInvalidValue;
+    // (sub-tiles of more than 4 fragments run a X + B X on BK = 64 only)
+    if constexpr (BK != 64 && (BM / WGM / 32) * (BN / WGN / 32) > 4) {
+        return hipErrorInvalidValue;
+    } else {
+        switch (kind) {
+            case GEMM_BX: k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX><<<grid, NT, 0, stream>>>(L, o); break;
+            case GEMM_BX_FINAL:
+                k_gemm_nt<BM, BN, BK, STAGES, WGM, WGN, GEMM_BX_FINAL><<<grid, NT, 0, stream>>>(L, o);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
-// The symmetric products only (for tiles no full-grid product uses).
+// The symmetric products only (tiles and engines a X + B X does not use).
 template <int BM, int BK, int STAGES>
 hipError_t launch_sym_t(GemmKind kind, const GemmLaunch& L, int blocks, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(blocks));
@@ -915,13 +930,8 @@ hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& la
     // 192 x 192 tiles of the symmetric products (2 x 2 waves of 96 x 96):
     // 4224 = 22 x 192 gives 253 upper tiles where 4096 = 16 x 256 gives 136
     if (tile == 192) return launch_sym_t<192, 64, 2>(kind, launch, blocks, stream);
-    // 256 x 256 tiles of a X + B X: 8 waves (2 x 4, each 128 x 64) by default,
-    // two per SIMD; MUON_BX_WAVES=4 selects the 4-wave engine (for tuning)
-    static const int bx_waves = [] {
-        const char* s = getenv("MUON_BX_WAVES");
-        return (s && atoi(s) == 4) ? 4 : 8;
-    }();
-    if (tile == 256 && bx_waves == 8 && (kind == GEMM_BX || kind == GEMM_BX_FINAL))
+    // 256 x 256 tiles of a X + B X: 8 waves (2 x 4, each 128 x 64), two per SIMD
+    if (tile == 256 && (kind == GEMM_BX || kind == GEMM_BX_FINAL))
         return launch_t<256, 256, 64, 2, 2, 4>(kind, launch, blocks, out, stream);
     // 256 x 256 tiles of X X^T: 8 waves (2 x 4, each 128 x 64; diagonal tiles
     // in 64 x 64 blocks); MUON_SYRK_WAVES=4 selects the 4-wave engine
@@ -953,9 +963,9 @@ hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& la
         case 128 * 4 + 1: return launch_t<128, 128, 32, 4>(kind, launch, blocks, out, stream);
         case 128 * 4 + 2: return launch_t<128, 128, 32, 2>(kind, launch, blocks, out, stream);
         case 64 * 4 + 2: return launch_t<64, 64, 32, 2>(kind, launch, blocks, out, stream);
-        case 256 * 4 + 2: return launch_t<256, 256, 64, 2>(kind, launch, blocks, out, stream);
-        case 256 * 4 + 0: return launch_t<256, 256, 64, 2>(kind, launch, blocks, out, stream);
-        case 256 * 4 + 1: return launch_t<256, 256, 32, 4>(kind, launch, blocks, out, stream);
+        case 256 * 4 + 2: return launch_sym_t<256, 64, 2>(kind, launch, blocks, stream);
+        case 256 * 4 + 0: return launch_sym_t<256, 64, 2>(kind, launch, blocks, stream);
+        case 256 * 4 + 1: return launch_sym_t<256, 32, 4>(kind, launch, blocks, stream);
         default: return hipErrorInvalidValue;
     }
 }
