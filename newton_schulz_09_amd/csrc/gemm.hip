@@ -272,8 +272,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<WGM, WGN, KIND>
     // the kernel arguments would wait on the scalar memory counter, which LDS
     // reads share
     const int64_t ldq = __builtin_amdgcn_readfirstlane(args.ldq);
+    // A diagonal tile of a symmetric product (ti == tj) reads the same rows
+    // as P and as Q: on 256 x 256 tiles with two stages its Q loads are
+    // skipped and its Q fragments come from the P tile.  (The waits of deeper
+    // pipelines count NLOAD loads per step; on smaller tiles the branch
+    // around each load cost more than the loads it saved: X X^T of the
+    // 1600-class matrices on 128 tiles took 3% longer.)
+    constexpr bool Q_SHARE = SYM && STAGES == 2 && BM == 256;
+    const bool q_is_p = Q_SHARE && ti == tj;
+    const int qoff = q_is_p ? 0 : BM * BK;  // where a stage's Q tile starts
     // load L (< IP: P rows, else Q rows) of K step kt into LDS stage `stage`
     auto issue_one = [&](int L, int kt, int stage) {
+        if (Q_SHARE && L >= IP && q_is_p) return;
         bf16_t* sP = lds + stage * STAGE;
         const int k0 = kt * BK;
         if (L < IP)
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<WGM, WGN, KIND>
         const int sl = (kt + STAGES - 1) % STAGES;
 
         const bf16_t* sP = lds + (kt % STAGES) * STAGE + wm * WTM * BK;
-        const bf16_t* sQ = lds + (kt % STAGES) * STAGE + BM * BK + wn * WTN * BK;
+        const bf16_t* sQ = lds + (kt % STAGES) * STAGE + qoff + wn * WTN * BK;
         const bf16_t* sQs_nn = lds + (kt % STAGES) * STAGE + BM * BK;  // NN: the whole Q tile
         bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
@@ -503,7 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<WGM, WGN, KIND>
             }
         }
         if constexpr (CAPTURE_E) {
-            const bf16_t* sQs = lds + (kt % STAGES) * STAGE + BM * BK;
+            const bf16_t* sQs = lds + (kt % STAGES) * STAGE + qoff;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int ik = i0 + wm * WTM + fm * 32;  // first K index of this fragment row block

@@ -202,6 +202,24 @@ def test_batched_mixed_shapes_equal_single_calls(muon):
         parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(host[k]), f"batched {shapes[k]}")
 
 
+def test_a_x_is_added_at_the_same_point_on_every_engine(muon):
+    """a X + B X adds a X[i][j] inside its K loop once the K values below the
+    end of row i's 64 block are summed, a point fixed by the row alone, so the
+    engine a matrix runs on does not change its result.  Alone, (256, 768),
+    (768, 256) and (768, 2304) run on 256 x 256 tiles (a X read from the stage
+    and added in the same K step) and (200, 520) (columns padded to 640) on
+    256 x 128 (a X copied out and added by the 64 x 64 wave sub-tiles); next to
+    (300, 768), whose rows pad to 384, all of them run on 128 x 128 tiles."""
+    shapes = [(256, 768), (768, 256), (768, 2304), (200, 520), (300, 768)]
+    rng = np.random.default_rng(2024)
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = muon.ns5_batched(Gs)
+    _bitwise_equal_to_single(muon, Gs, outs)
+    for k in (0, 3):
+        parity.assert_ns5_parity(parity.to_np(outs[k]), oracle.ns5(host[k]), f"{shapes[k]} next to (300, 768)")
+
+
 def test_batched_many_shapes_and_passes(muon):
     """More than 8 distinct shapes and more than 128 matrices: the batch runs
     in several launch groups and passes over one workspace."""
