@@ -87,8 +87,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "aaad5649e3f58b03a243ac0b3092f761aafbac232fe31cf1b158a96e55a45f68",
-    "fetch_bytes": 391655411,
+    "sources_sha256": "dc5a66c9eabab4d62a2a812002bab495325037489d951ce6210400555ab8c089",
+    "fetch_bytes": 285523385,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
