@@ -158,17 +158,18 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // Waves per SIMD the register allocation must leave room for.  4-wave
-// a X + B X workgroups ask for two: within that budget the MFMA accumulators
-// live in ordinary VGPRs, which the a X update inside the K loop writes
-// directly (with a budget of one wave per SIMD they go to AGPRs, and every K
-// step copies them out and back).
-template <int WGM, int WGN, int KIND>
+// a X + B X workgroups whose LDS lets two of them share a CU ask for two:
+// within that budget the MFMA accumulators live in ordinary VGPRs, which the
+// a X update inside the K loop writes directly (with a budget of one wave per
+// SIMD they go to AGPRs, and every K step copies them out and back).
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KIND>
 constexpr int min_waves_per_simd() {
-    return (WGM * WGN == 4 && (KIND == GEMM_BX || KIND == GEMM_BX_FINAL)) ? 2 : 1;
+    constexpr bool two_fit = 2 * STAGES * (BM + BN) * BK * 2 <= 160 * 1024;  // two workgroups' LDS per CU
+    return (WGM * WGN == 4 && two_fit && (KIND == GEMM_BX || KIND == GEMM_BX_FINAL)) ? 2 : 1;
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KIND>
-__global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<WGM, WGN, KIND>())) void k_gemm_nt(
+__global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<BM, BN, BK, STAGES, WGM, WGN, KIND>())) void k_gemm_nt(
     GemmLaunch launch, PtrTable out) {
     constexpr bool SYM = (KIND == GEMM_SYRK || KIND == GEMM_AAB);
     static_assert(!SYM || BM == BN, "symmetric products use square tiles");
