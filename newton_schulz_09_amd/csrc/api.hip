@@ -41,11 +41,14 @@ int hip_fail(hipError_t e, const char* where) {
 inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// GEMM tile edge for the short side m.  Padding m and n to the tile keeps the
-// GEMMs free of edge handling; the choice trades padded work against the
-// larger tile's better operand reuse.  MUON_NS5_TILE=64/128/256 in the
-// environment forces one edge for every shape (read once, for tuning sweeps).
-int choose_tile(int64_t m) {
+int device_cus();
+
+// GEMM tile edge for the short side m of `count` m x n matrices.  Padding m
+// and n to the tile keeps the GEMMs free of edge handling; the choice trades
+// padded work against the larger tile's better operand reuse.
+// MUON_NS5_TILE=64/128/256 in the environment forces one edge for every
+// shape (read once, for tuning sweeps).
+int choose_tile(int64_t m, int64_t n, int64_t count) {
     static const int forced = [] {
         const char* s = getenv("MUON_NS5_TILE");
         const int t = s ? atoi(s) : 0;
@@ -53,11 +56,20 @@ int choose_tile(int64_t m) {
     }();
     if (forced) return forced;
     if (m <= 64) return 64;
-    // 256-wide tiles reuse each operand panel twice as much but give a
-    // quarter of the workgroups: below m = 2048 the 128 tile fills the 256
-    // CUs better (measured on the 768- and 1600-class shapes)
-    if (m < 2048) return 128;
-    return 256;
+    if (m >= 2048) return 256;
+    // Below m = 2048 the 128 tile, whose extra workgroups fill the CUs
+    // better; where its padded m is a multiple of 256, X X^T and a X + B X
+    // still run on 256 x 256 tiles.  Where it is not, 256 tiles over m padded
+    // to 256 are taken if that pads m by at most 8% more and the batch gives
+    // a X + B X two rounds of the device's CUs or more: every product then
+    // runs on the 256 engines, whose operand reuse outweighs the padding
+    // (the GPT-2 1.5B set, m = 1600: 54.3 -> 51.5 ms per step).
+    const int64_t mp128 = round_up(m, 128), mp256 = round_up(m, 256);
+    if (mp128 % 256 != 0 && mp256 * 100 <= mp128 * 108) {
+        const int64_t c = count < kMaxGroup ? count : kMaxGroup;
+        if (c * (mp256 / 256) * (round_up(n, 256) / 256) >= 2 * static_cast<int64_t>(device_cus())) return 256;
+    }
+    return 128;
 }
 
 // Row skew (elements) added to every workspace row stride: 64 bf16 = 128
@@ -194,7 +206,7 @@ bool make_plan(int64_t rows, int64_t cols, int64_t count, Ns5Plan* p) {
     p->m = static_cast<int>(m);
     p->n = static_cast<int>(n);
     p->tall = rows > cols;
-    p->tile = choose_tile(m);
+    p->tile = choose_tile(m, n, count);
     p->mp = static_cast<int>(round_up(m, p->tile));
     p->np = static_cast<int>(round_up(n, p->tile));
     int64_t nb = (rows * cols + 16383) / 16384;
