@@ -4,7 +4,8 @@
 //     A = X X^T              (SYRK: upper-triangle tiles only, mirrored)
 //     B = b A + c A A        (A is symmetric, so A A = A A^T; upper tiles,
 //                             mirrored; the b A + c (.) update is fused)
-//     X' = a X + B X         (full tile grid; a X + (.) fused; X' is stored
+//     X' = a X + B X         (full tile grid; a X is added inside the K loop
+//                             from the X rows staged there; X' is stored
 //                             row-major for the next step, or as float32 in
 //                             G's orientation after the last step)
 //
@@ -47,8 +48,9 @@
 // panel of the second operand is read from memory once); for the symmetric
 // products, whose K differs between segments, whole matrices are dealt to
 // the XCDs in turn.  The mapping only places work: every output element is
-// accumulated in the same K order under any tile shape or mapping, so a
-// matrix gets bitwise the same result in any batch.
+// accumulated in the same K order under any tile shape or mapping (and a X
+// enters the sum at the same K), so a matrix gets bitwise the same result in
+// any batch.
 #include <stdlib.h>
 
 #include <type_traits>
