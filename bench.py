@@ -87,8 +87,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "21242be230dccf3858710d8f05fc1dbc8a9ed40a99fd3f8e5e5f58ba79507d42",
-    "fetch_bytes": 285530073,
+    "sources_sha256": "e9fc05426c05161b3d501953f0a21db0c3e73447c7a2bd3c4e982a238c118cb7",
+    "fetch_bytes": 285452465,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
