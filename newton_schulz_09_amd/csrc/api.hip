@@ -43,6 +43,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 int device_cus();
 
+// X' bytes of one a X + B X launch from which it stores X' with streaming
+// stores (set between the sizes measured either way: 34 MB and 170 MB)
+constexpr int64_t kStreamOutBytes = int64_t{96} << 20;
+
 // GEMM tile edge for the short side m of `count` m x n matrices.  Padding m
 // and n to the tile keeps the GEMMs free of edge handling; the choice trades
 // padded work against the larger tile's better operand reuse.
@@ -601,6 +605,15 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                     if (L->seg[ci].tiles_per_mat != tpm) tpm = 0;
                 L->interleave_tpm = tpm;
             }
+            // X' of a large launch goes out with streaming stores, so that it
+            // does not displace the operands its tiles share in the caches;
+            // a small one (that the next X X^T finds in the caches) does not:
+            // measured on one box, the 124M set (170 MB of X') gained 13 us
+            // per step, one 4096^2 matrix (34 MB) lost 2%
+            int64_t x_bytes = 0;
+            for (const Chunk& c : grp.chunks)
+                x_bytes += static_cast<int64_t>(c.plan.x_elems) * c.plan.cnt * 2;
+            bx.stream_out = x_bytes >= kStreamOutBytes ? 1 : 0;
             e = launch_gemm(GEMM_SYRK, syrk_tile, syrk_tile, syrk, nb_syrk, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "X X^T launch");
             const int aab_tile = grp.chunks[0].plan.sym_tile;

@@ -729,7 +729,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (min_waves_per_simd<BM, BN, BK, STA
             const int row = q / cpr, c = q % cpr;
             const u32x4 v =
                 *reinterpret_cast<const u32x4*>(W + row * cpr * 8 + (eslot<cpr>(c, row >> shift) << 3));
-            *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(row) * ld + c * 8) = v;
+            u32x4* d = reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(row) * ld + c * 8);
+            if (KIND == GEMM_BX && launch.stream_out)
+                __builtin_nontemporal_store(v, d);
+            else
+                *d = v;
         }
     };
 

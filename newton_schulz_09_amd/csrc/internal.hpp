@@ -103,6 +103,8 @@ struct GemmLaunch {
     // are dealt round-robin over the XCDs (balances segments whose K
     // differs); 0: each XCD takes one contiguous range of the grid
     int interleave_tpm;
+    // a X + B X only: 1 stores X' with streaming (non-temporal) stores
+    int stream_out;
 };
 
 hipError_t launch_momentum(const float* g, float* buf, float* u, int64_t numel, float mu,
