@@ -528,3 +528,25 @@ def test_two_4096_matrices_equal_single_calls(muon):
     for k, G in enumerate(Gs):
         assert torch.equal(outs[k], muon.ns5(G)), k
         assert torch.isfinite(outs[k]).all()
+
+
+@pytest.mark.parametrize("shapes", [
+    # 16 x 36 upper 256 tiles in X X^T and b A + c A A (2.25 rounds of 256
+    # CUs); alone, a 2048^2 matrix takes 192 tiles for them
+    [(2048, 2048)] * 16,
+    # three segments, two K lengths in X X^T (2048 and 4096), tall matrices
+    [(2048, 2048)] * 12 + [(2048, 4096)] * 6 + [(4096, 2048)] * 6,
+], ids=["16x2048^2", "mixed-K"])
+def test_batches_of_2048_class_matrices_equal_single_calls(muon, shapes):
+    """Batches of 2048-class matrices, whose symmetric products run several
+    rounds of 256 x 256 tiles, give every matrix bitwise what a single call
+    (192 tiles for a lone 2048^2) gives it, the same on every call."""
+    rng = np.random.default_rng(77)
+    host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host]
+    outs = muon.ns5_batched(Gs)
+    again = muon.ns5_batched(Gs)
+    for k, (a, b) in enumerate(zip(outs, again)):
+        assert torch.equal(a, b), f"matrix {k} differs between two calls"
+        assert torch.isfinite(a).all(), k
+    _bitwise_equal_to_single(muon, Gs, outs)
