@@ -87,8 +87,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "e9fc05426c05161b3d501953f0a21db0c3e73447c7a2bd3c4e982a238c118cb7",
-    "fetch_bytes": 285452465,
+    "sources_sha256": "b2a9ac75dbf9a7b4bb9bf35152c4ac15e631b2dd4bd3cfbe2e86f7bcfedcbc33",
+    "fetch_bytes": 285760245,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
