@@ -87,8 +87,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "b2a9ac75dbf9a7b4bb9bf35152c4ac15e631b2dd4bd3cfbe2e86f7bcfedcbc33",
-    "fetch_bytes": 285760245,
+    "sources_sha256": "c2ab2926691a95d41bf9c055b1ae7e8750b8de7474cadf8336fdb07f2b82cb1d",
+    "fetch_bytes": 285480004,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",

@@ -44,6 +44,13 @@ typedef enum muon_status {
     MUON_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed  */
 } muon_status;
 
+/* Element type of G and out in muon_ns5 / muon_ns5_grouped: float32, or
+ * bfloat16 (uint16_t bit patterns).  The iteration is bf16 either way. */
+typedef enum muon_dtype {
+    MUON_F32 = 0,
+    MUON_BF16 = 1
+} muon_dtype;
+
 /* Quintic coefficients of p(x) = a x + b x^3 + c x^5 (the printed listing);
  * the kernels use their float32 values. */
 #define MUON_NS5_A 3.4445f
@@ -107,41 +114,46 @@ size_t muon_ns5_workspace_size(int64_t rows, int64_t cols, int64_t count);
 
 /*
  * NS5 of one matrix (the printed zeroth_power_via_newtonschulz5):
- *     X = bf16( bf16(G) / (||G||_F + eps) )         norm of the fp32 input
+ *     X = bf16( bf16(G) / (||G||_F + eps) )         norm of the input
  *     if rows > cols: X = X^T                        iterate on the short side
  *     repeat `steps` times:
  *         A = bf16( X X^T )                          bf16 MFMA, fp32 accumulate
  *         B = bf16( b A + c A A )
  *         X = bf16( a X + B X )
- *     out = float32( rows > cols ? X^T : X )
+ *     out = (G's type)( rows > cols ? X^T : X )
  * with (a, b, c) = (MUON_NS5_A, MUON_NS5_B, MUON_NS5_C).
- *  G    : [rows x cols] float32, read only.
- *  out  : [rows x cols] float32, written (every value is bf16-representable);
- *         may alias G.
+ *  G    : [rows x cols] of `dtype`, read only.
+ *  out  : [rows x cols] of `dtype`, written; may alias G.  float32: every
+ *         value is bf16-representable; bfloat16: the last iterate as is (the
+ *         same values).  For bfloat16 G the first cast is exact, and the norm
+ *         is that of the bf16 values.
  *  rows, cols : >= 1, min <= MUON_NS5_MAX_SHORT, max <= MUON_NS5_MAX_LONG.
+ *  dtype: MUON_F32 or MUON_BF16.
  *  steps: >= 0 (0 returns the normalised, bf16-rounded input).
  *  eps  : > 0 is typical; any finite value is accepted.
- *  workspace, workspace_bytes: >= muon_ns5_workspace_size(rows, cols, 1).
- * Errors: MUON_ERR_INVALID_ARG (null pointer, rows/cols < 1, steps < 0,
- * eps not finite), MUON_ERR_UNSUPPORTED (sizes beyond the limits),
- * MUON_ERR_WORKSPACE (workspace null, misaligned or too small).
+ *  workspace, workspace_bytes: >= muon_ns5_workspace_size(rows, cols, 1)
+ *         (the same for either dtype).
+ * Errors: MUON_ERR_INVALID_ARG (null pointer, rows/cols < 1, an unknown
+ * dtype, steps < 0, eps not finite), MUON_ERR_UNSUPPORTED (sizes beyond the
+ * limits), MUON_ERR_WORKSPACE (workspace null, misaligned or too small).
  */
-int muon_ns5(const float* G, float* out, int64_t rows, int64_t cols, int steps, float eps,
+int muon_ns5(const void* G, void* out, int64_t rows, int64_t cols, muon_dtype dtype, int steps, float eps,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * NS5 of `count` independent matrices of the same shape, batched so that each
- * kernel launch covers every matrix of a pass (up to MUON_NS5_MAX_GROUP).
- *  G, out : host arrays of `count` device pointers; out[i] may alias G[i];
- *           distinct i must not overlap.
+ * NS5 of `count` independent matrices of the same shape and type, batched so
+ * that each kernel launch covers every matrix of a pass (up to
+ * MUON_NS5_MAX_GROUP).
+ *  G, out : host arrays of `count` device pointers to `dtype` matrices;
+ *           out[i] may alias G[i]; distinct i must not overlap.
  *  count  : >= 1.
  *  Everything else as in muon_ns5, with workspace_bytes >=
  *  muon_ns5_workspace_size(rows, cols, count).
  * Errors: as muon_ns5, plus MUON_ERR_INVALID_ARG for count < 1 or a null
  * entry in G or out.
  */
-int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows,
-                     int64_t cols, int steps, float eps, void* workspace, size_t workspace_bytes,
+int muon_ns5_grouped(const void* const* G, void* const* out, int64_t count, int64_t rows, int64_t cols,
+                     muon_dtype dtype, int steps, float eps, void* workspace, size_t workspace_bytes,
                      void* stream);
 
 /*

@@ -1104,18 +1104,24 @@ size_t muon_ns5_batched_workspace_size(const int64_t* rows, const int64_t* cols,
     return st ? 0 : groups_bytes(groups);
 }
 
-int muon_ns5(const float* G, float* out, int64_t rows, int64_t cols, int steps, float eps, void* workspace,
-             size_t workspace_bytes, void* stream) {
+int muon_ns5(const void* G, void* out, int64_t rows, int64_t cols, muon_dtype dtype, int steps, float eps,
+             void* workspace, size_t workspace_bytes, void* stream) {
     using namespace muon;
     if (!G || !out) return fail(MUON_ERR_INVALID_ARG, "null G or out");
-    return muon_ns5_grouped(&G, &out, 1, rows, cols, steps, eps, workspace, workspace_bytes, stream);
+    return muon_ns5_grouped(&G, &out, 1, rows, cols, dtype, steps, eps, workspace, workspace_bytes, stream);
 }
 
-int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, int64_t rows, int64_t cols,
-                     int steps, float eps, void* workspace, size_t workspace_bytes, void* stream) {
+int muon_ns5_grouped(const void* const* G, void* const* out, int64_t count, int64_t rows, int64_t cols,
+                     muon_dtype dtype, int steps, float eps, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     using namespace muon;
+    if (dtype != MUON_F32 && dtype != MUON_BF16)
+        return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    // the pointer tables carry addresses only; the kernels read and write
+    // the element type the update names
     Segment sg;
-    int st = grouped_segment(G, out, count, rows, cols, &sg);
+    int st = grouped_segment(reinterpret_cast<const float* const*>(G), reinterpret_cast<float* const*>(out), count,
+                             rows, cols, &sg);
     if (st) return st;
     st = check_common(steps, eps);
     if (st) return st;
@@ -1124,7 +1130,9 @@ int muon_ns5_grouped(const float* const* G, float* const* out, int64_t count, in
     if (st) return st;
     st = check_workspace(workspace, workspace_bytes, groups_bytes(groups));
     if (st) return st;
-    return run_groups(groups, kQuintic, Update{}, 0.0f, steps, eps, static_cast<char*>(workspace),
+    Update up;
+    up.bf16_io = dtype == MUON_BF16;
+    return run_groups(groups, kQuintic, up, 0.0f, steps, eps, static_cast<char*>(workspace),
                       static_cast<hipStream_t>(stream), nullptr);
 }
 

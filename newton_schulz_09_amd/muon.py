@@ -19,6 +19,9 @@ MUON_ERR_INVALID_ARG = 1
 MUON_ERR_UNSUPPORTED = 2
 MUON_ERR_WORKSPACE = 3
 MUON_ERR_HIP = 4
+# muon_dtype: the element type of muon_ns5 / muon_ns5_grouped
+MUON_F32 = 0
+MUON_BF16 = 1
 
 NS5_STEPS = 5
 NS5_EPS = 1e-7
@@ -64,10 +67,10 @@ def _load():
     lib.muon_momentum_nesterov_grouped.restype = ctypes.c_int
     lib.muon_ns5_workspace_size.argtypes = [i64, i64, i64]
     lib.muon_ns5_workspace_size.restype = sz
-    lib.muon_ns5.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+    lib.muon_ns5.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.muon_ns5.restype = ctypes.c_int
     lib.muon_ns5_grouped.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
-                                     ctypes.c_float, vp, sz, vp]
+                                     ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.muon_ns5_grouped.restype = ctypes.c_int
     pi64 = ctypes.POINTER(i64)
     lib.muon_ns5_batched_workspace_size.argtypes = [pi64, pi64, i64]
@@ -203,16 +206,25 @@ def _workspace(device, stream, nbytes):
     return ws
 
 
+def _dtype_code(t):
+    """muon_dtype of a float32 or bfloat16 tensor (others are rejected by
+    the checks that follow)."""
+    return MUON_BF16 if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16 else MUON_F32
+
+
 def ns5(G, out=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
-    """Quintic Newton-Schulz orthogonalisation of one 2-D float32 matrix.
+    """Quintic Newton-Schulz orthogonalisation of one 2-D float32 or
+    bfloat16 matrix; ``out`` has G's type (bfloat16: the last iterate as is).
     Returns ``out`` (a new tensor unless given; may be ``G``)."""
-    _require_f32_cuda(G, "G")
+    code = _dtype_code(G)
+    dtype = torch.bfloat16 if code == MUON_BF16 else torch.float32
+    _require_f32_cuda(G, "G", dtype)
     if G.dim() != 2:
         raise ValueError("G must be 2-D")
     rows, cols = G.shape
     if out is None:
         out = torch.empty_like(G)
-    _require_f32_cuda(out, "out")
+    _require_f32_cuda(out, "out", dtype)
     if out.shape != G.shape or out.device != G.device:
         raise ValueError("out must have G's shape and device")
     need = workspace_size(rows, cols, 1)
@@ -220,23 +232,26 @@ def ns5(G, out=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
         raise MuonError(MUON_ERR_UNSUPPORTED, f"shape {rows}x{cols} is not supported")
     stream = _stream_handle(G.device)
     ws = workspace if workspace is not None else _workspace(G.device, stream, need)
-    _check(lib.muon_ns5(G.data_ptr(), out.data_ptr(), rows, cols, int(steps), float(eps), ws.data_ptr(),
+    _check(lib.muon_ns5(G.data_ptr(), out.data_ptr(), rows, cols, code, int(steps), float(eps), ws.data_ptr(),
                         ws.numel() * ws.element_size(), stream))
     return out
 
 
 def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
-    """NS5 of a list of same-shaped float32 matrices, batched per launch.
-    Returns the list of outputs (new tensors unless given)."""
+    """NS5 of a list of same-shaped matrices, all float32 or all bfloat16,
+    batched per launch.  Returns the list of outputs (new tensors unless
+    given), of the inputs' type."""
     Gs = list(Gs)
     if not Gs:
         return []
+    code = _dtype_code(Gs[0])
+    dtype = torch.bfloat16 if code == MUON_BF16 else torch.float32
     for i, G in enumerate(Gs):
-        _require_f32_cuda(G, f"Gs[{i}]")
+        _require_f32_cuda(G, f"Gs[{i}]", dtype)
     shape, device = Gs[0].shape, Gs[0].device
     if len(shape) != 2 or any(G.shape != shape or G.device != device for G in Gs):
         raise ValueError("all matrices must be 2-D with the same shape and device")
-    outs = _outputs(Gs, outs)
+    outs = _outputs(Gs, outs, dtype)
     rows, cols = shape
     count = len(Gs)
     need = workspace_size(rows, cols, count)
@@ -246,7 +261,7 @@ def ns5_grouped(Gs, outs=None, steps=NS5_STEPS, eps=NS5_EPS, workspace=None):
     ws = workspace if workspace is not None else _workspace(device, stream, need)
     g_ptrs = (ctypes.c_void_p * count)(*[G.data_ptr() for G in Gs])
     o_ptrs = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
-    _check(lib.muon_ns5_grouped(g_ptrs, o_ptrs, count, rows, cols, int(steps), float(eps), ws.data_ptr(),
+    _check(lib.muon_ns5_grouped(g_ptrs, o_ptrs, count, rows, cols, code, int(steps), float(eps), ws.data_ptr(),
                                 ws.numel() * ws.element_size(), stream))
     return outs
 

@@ -38,7 +38,19 @@ int main(void) {
     expect(muon_momentum_nesterov(NULL, (float*)fake, (float*)fake, 4, 0.95f, NULL) == MUON_ERR_INVALID_ARG,
            "null gradient");
     expect(muon_momentum_nesterov_grouped(NULL, NULL, NULL, NULL, 0, 0.95f, NULL) == MUON_OK, "empty group");
-    expect(muon_ns5(NULL, (float*)fake, 64, 128, 5, 1e-7f, fake, 1 << 20, NULL) == MUON_ERR_INVALID_ARG, "null G");
+    expect(muon_ns5(NULL, fake, 64, 128, MUON_F32, 5, 1e-7f, fake, 1 << 20, NULL) == MUON_ERR_INVALID_ARG, "null G");
+    expect(muon_ns5(fake, fake, 64, 128, (muon_dtype)7, 5, 1e-7f, fake, 1 << 20, NULL) == MUON_ERR_INVALID_ARG,
+           "unknown dtype");
+    {
+        const void* gv[2] = {g2[0], g2[1]};
+        void* ov[2] = {o2[0], o2[1]};
+        expect(muon_ns5_grouped(gv, ov, 2, 64, 128, MUON_BF16, 5, 1e-7f, (void*)0x200000, 256, NULL) ==
+                   MUON_ERR_WORKSPACE,
+               "bf16 group with a small workspace");
+        expect(muon_ns5_grouped(gv, ov, 0, 64, 128, MUON_BF16, 5, 1e-7f, (void*)0x200000, 1 << 20, NULL) ==
+                   MUON_ERR_INVALID_ARG,
+               "empty group");
+    }
     expect(muon_ns5_batched(g2, o2, rows, cols, 2, 5, 1e-7f, (void*)0x200000, need - 256, NULL) == MUON_ERR_WORKSPACE,
            "small workspace");
     expect(muon_ns5_batched(g2, o2, rows, cols, 2, -1, 1e-7f, (void*)0x200000, need, NULL) == MUON_ERR_INVALID_ARG,

@@ -75,25 +75,30 @@ def test_validation_errors_before_any_launch(muon):
     assert b"alias" in lib.muon_last_error()
     # ns5
     need = muon.workspace_size(64, 128, 1)
-    assert lib.muon_ns5(None, fake, 64, 128, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5(fake, fake, 0, 128, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5(fake, fake, 64, 128, -1, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5(fake, fake, 64, 128, 5, float("nan"), ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, None, need, None) == muon.MUON_ERR_WORKSPACE
-    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, ctypes.c_void_p(0x200010), need, None) \
+    assert lib.muon_ns5(None, fake, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 0, 128, muon.MUON_F32, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_F32, -1, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_F32, 5, float("nan"), ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_F32, 5, 1e-7, None, need, None) == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_F32, 5, 1e-7, ctypes.c_void_p(0x200010), need, None) \
         == muon.MUON_ERR_WORKSPACE
-    assert lib.muon_ns5(fake, fake, 64, 128, 5, 1e-7, ws_small, need - 1, None) == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need - 1, None) == muon.MUON_ERR_WORKSPACE
     assert b"needed" in lib.muon_last_error()
-    assert lib.muon_ns5(fake, fake, 1 << 15, 1 << 15, 5, 1e-7, ws_small, 1 << 40, None) \
+    assert lib.muon_ns5(fake, fake, 64, 128, 2, 5, 1e-7, ws_small, need, None) == muon.MUON_ERR_INVALID_ARG
+    assert b"dtype" in lib.muon_last_error()
+    # a bf16 matrix needs the same workspace
+    assert lib.muon_ns5(fake, fake, 64, 128, muon.MUON_BF16, 5, 1e-7, ws_small, need - 1, None) \
+        == muon.MUON_ERR_WORKSPACE
+    assert lib.muon_ns5(fake, fake, 1 << 15, 1 << 15, muon.MUON_F32, 5, 1e-7, ws_small, 1 << 40, None) \
         == muon.MUON_ERR_UNSUPPORTED
     # grouped
     arr = (ctypes.c_void_p * 2)(0x100000, 0)
     ok = (ctypes.c_void_p * 2)(0x100000, 0x100100)
     need2 = muon.workspace_size(64, 128, 2)
-    assert lib.muon_ns5_grouped(ok, arr, 2, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5_grouped(ok, ok, 0, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5_grouped(None, ok, 2, 64, 128, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
-    assert lib.muon_ns5_grouped(ok, ok, 2, 64, 128, 5, 1e-7, ws_small, need2 - 256, None) \
+    assert lib.muon_ns5_grouped(ok, arr, 2, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(ok, ok, 0, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(None, ok, 2, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need2, None) == muon.MUON_ERR_INVALID_ARG
+    assert lib.muon_ns5_grouped(ok, ok, 2, 64, 128, muon.MUON_F32, 5, 1e-7, ws_small, need2 - 256, None) \
         == muon.MUON_ERR_WORKSPACE
 
 

@@ -474,6 +474,27 @@ def test_bf16_inputs_give_bf16_outputs(muon, steps):
             assert d.max() <= 1 and np.mean(d == 0) >= 0.999
 
 
+def test_single_and_grouped_calls_take_bf16(muon):
+    """muon_ns5 and muon_ns5_grouped with MUON_BF16: bitwise what the batched
+    bf16 entry point (checked against the oracle above) gives the same
+    matrices, with bf16 outputs; in place too."""
+    rng = np.random.default_rng(16)
+    one = torch.from_numpy(rng.standard_normal((96, 200)).astype(np.float32)).to("cuda").to(torch.bfloat16)
+    got = muon.ns5(one)
+    assert got.dtype == torch.bfloat16
+    assert torch.equal(got, muon.ns5_batched([one])[0])
+    group = [torch.from_numpy(rng.standard_normal((300, 130)).astype(np.float32)).to("cuda").to(torch.bfloat16)
+             for _ in range(5)]
+    outs = muon.ns5_grouped(group)
+    want = muon.ns5_batched(group)
+    for k in range(len(group)):
+        assert outs[k].dtype == torch.bfloat16 and torch.equal(outs[k], want[k]), k
+    inplace = [g.clone() for g in group]
+    muon.ns5_grouped(inplace, outs=inplace)
+    for k in range(len(group)):
+        assert torch.equal(inplace[k], want[k]), k
+
+
 # ---------------------------------------------------------------- grouped momentum
 
 def test_momentum_grouped_ragged_misaligned_and_passes(muon):
