@@ -353,17 +353,32 @@ def _loaded_step(torch, step, workloads):
 
 def cpu_samples(workloads):
     """The oracle on bounded samples of the other workloads, each scaled to
-    its whole size: the 64x128 step and its transpose whole; one matrix of
-    each of the four GPT-2 1.5B shape classes (momentum + NS5), scaled by 48;
-    one 2048x8192 and one 8192x2048 matrix (NS5), scaled by 8."""
+    its whole size: the 64x128 step and its transpose whole (median of 3);
+    the 4096x4096 NS5 from its normalisation and one step, scaled to five
+    steps; one matrix of each of the four GPT-2 1.5B shape classes
+    (momentum + NS5), scaled by 48; one 2048x8192 and one 8192x2048 matrix
+    (NS5), scaled by 8."""
     import oracle
     res = {}
     G, buf = workloads.single_64x128()
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for M, B in ((G, buf), (G.T, buf.T)):
+            _, u = oracle.momentum_nesterov(M, B, 0.95)
+            oracle.ns5(u)
+        runs.append(time.perf_counter() - t0)
+    res["single_64x128_ms"] = round(sorted(runs)[1] * 1e3, 2)
+    G, _, _, _ = workloads.square_4096()
     t0 = time.perf_counter()
-    for M, B in ((G, buf), (G.T, buf.T)):
-        _, u = oracle.momentum_nesterov(M, B, 0.95)
-        oracle.ns5(u)
-    res["single_64x128_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+    oracle.ns5(G, steps=0)
+    t_norm = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.ns5(G, steps=1)
+    t_one = time.perf_counter() - t0
+    res["square_4096_s"] = round(t_norm + 5 * (t_one - t_norm), 1)
+    res["square_4096_sample"] = (f"the normalisation alone ({t_norm:.1f} s) and with one NS5 step ({t_one:.1f} s): "
+                                 f"normalisation + 5 steps")
     t0 = time.perf_counter()
     for si in range(4):
         _, _, G, buf = workloads.gpt_hidden_set(workloads.GPT2_1P5B_SHAPES, 1, 4, only_shape=si)[0]
