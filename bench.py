@@ -484,6 +484,9 @@ def main():
     }
     symmin = sum(sym_min_flops(r, c) for r, c in st.shapes)
     res["pct_mfma_peak_symmetric_min"] = round(100 * symmin / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
+    props = torch.cuda.get_device_properties(0)
+    res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                     "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1)}
     if not args.skip_extras:
         res["roofline"] = time_dominant_kernel(st, args.steps, torch)
         log(f"dominant kernel: {res['roofline']}")
