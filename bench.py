@@ -80,8 +80,10 @@ def parse():
 COPY_BYTES = 1 << 30
 
 # HBM-side traffic of the dominant kernel per launch, from two rocprofv3 --pmc
-# runs over `bench.py --steps 2 --warmup 1 --skip-extras` (FETCH_SIZE, then
-# WRITE_SIZE, in KiB per dispatch), scaled by what the same counters read for
+# runs over `MUON_SPLIT=0 bench.py --steps 2 --warmup 1 --skip-extras` (the
+# step on one stream, so that it runs the launch over all 48 matrices;
+# FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), scaled by what the same
+# counters read for
 # the 1 GiB copy of `bench.py --copy-calibration` (FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0).  Valid only for the kernel sources it was measured with:
 # reported as null once their hash differs (the summary is
@@ -139,8 +141,11 @@ def time_step(st, steps, torch):
 
 def time_dominant_kernel(st, steps, torch):
     """Second timed pass: the same steps, with HIP events recorded by the
-    library around every a X + B X launch of NS5 steps 1-4 (each launch covers
-    all 48 matrices)."""
+    library around every a X + B X launch of NS5 steps 1-4, each launch over
+    all 48 matrices: the kernel measured alone (the library's measurement
+    hook keeps the whole batch on the caller's stream; the timed step runs
+    every product as two launches of 24 matrices on two streams, whose
+    durations overlap other work)."""
     max_pairs = 4 * (st.steps - 1)      # room for several launch groups
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * max_pairs)] for _ in range(steps)]
     for evs in events:                  # create the underlying HIP events
@@ -166,7 +171,7 @@ def time_dominant_kernel(st, steps, torch):
     return {
         "bound": "mfma",
         "kernel": "k_gemm_nt<256, 256, 64, 2, 2, 4, GEMM_BX> (256x256 tiles, 8 waves): X' = a X + B X of NS5 steps 1-4, one launch over all "
-                  "48 matrices",
+                  "48 matrices, measured alone (the step runs it as two concurrent launches of 24)",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
