@@ -89,8 +89,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "c2ab2926691a95d41bf9c055b1ae7e8750b8de7474cadf8336fdb07f2b82cb1d",
-    "fetch_bytes": 285480004,
+    "sources_sha256": "57795141fc3d25bba86aa7365c9659ae0bb453554fe07b65b5a2f01c45879d38",
+    "fetch_bytes": 285905603,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
