@@ -144,7 +144,7 @@ def time_dominant_kernel(st, steps, torch):
     library around every a X + B X launch of NS5 steps 1-4, each launch over
     all 48 matrices: the kernel measured alone (the library's measurement
     hook keeps the whole batch on the caller's stream; the timed step runs
-    every product as two launches of 24 matrices on two streams, whose
+    every product as three launches of 16 matrices on three streams, whose
     durations overlap other work)."""
     max_pairs = 4 * (st.steps - 1)      # room for several launch groups
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * max_pairs)] for _ in range(steps)]
@@ -171,7 +171,7 @@ def time_dominant_kernel(st, steps, torch):
     return {
         "bound": "mfma",
         "kernel": "k_gemm_nt<256, 256, 64, 2, 2, 4, GEMM_BX> (256x256 tiles, 8 waves): X' = a X + B X of NS5 steps 1-4, one launch over all "
-                  "48 matrices, measured alone (the step runs it as two concurrent launches of 24)",
+                  "48 matrices, measured alone (the step runs it as three concurrent launches of 16)",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",

@@ -16,14 +16,15 @@
  *    array the library holds as its workspace).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is ordered on it and the call returns without synchronising.  A
- *    batched call over a large single-group batch (at least 4 matrices and
- *    5e11 nominal NS5 flops) runs its second half on a side stream the
- *    library creates once per device (default priority, not synchronising
- *    with the null stream), forked from and joined back into `stream` with
- *    events, so the work still begins after everything enqueued on `stream`
- *    before the call and ends before anything enqueued after it; this holds
- *    under graph capture too.  Batched calls enqueue under a process-wide
- *    lock.
+ *    batched call over a large single-group batch (at least 5e11 nominal
+ *    NS5 flops and 2 matrices per part) runs as 2 or 3 parts, every part but
+ *    the first on a side stream the library creates once per device (default
+ *    priority, not synchronising with the null stream), forked from and
+ *    joined back into `stream` with events, so the work still begins after
+ *    everything enqueued on `stream` before the call and ends before
+ *    anything enqueued after it; this holds under graph capture too.
+ *    Results do not depend on the split.  Batched calls enqueue under a
+ *    process-wide lock.
  *  - Arguments are validated before anything is enqueued; a validation error
  *    returns a non-zero status and enqueues nothing.  A HIP launch error is
  *    reported as MUON_ERR_HIP; faults during execution surface at the

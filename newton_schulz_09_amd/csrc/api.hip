@@ -718,121 +718,150 @@ int batched_segments(const float* const* G, float* const* out, float* const* buf
     return MUON_OK;
 }
 
-// Two-stream schedule of a large batch.  The step's prologue (momentum and
+// Multi-stream schedule of a large batch.  The step's prologue (momentum and
 // the norm, then the cast) streams HBM while the products keep the matrix
-// cores busy, so a batch runs as two halves: the first on the caller's
-// stream, the second on a side stream the library keeps per device, started
-// once the first half's prologue is done, so that each half's prologue
-// overlaps the other half's products.  Every segment's matrices are dealt
-// alternately to the halves (both get the same mix of shapes).  Each half is
-// an ordinary batch, so every matrix gets bitwise what it gets alone.
-// Measured on one box (two runs each): the GPT-2 124M step 1.785/1.790 ->
-// 1.739/1.730 ms, the 16 extreme-aspect matrices 9.55 -> 9.19 ms.  Taken for
-// a batch of one launch group with at least 4 matrices and 5e11 nominal
-// flops.  MUON_SPLIT=0 turns it off (for tuning).
+// cores busy, so a batch runs as K parts: the first on the caller's stream,
+// part p on side stream p of the library (kept per device), started once part
+// p - 1's prologue is done, so that each part's prologue overlaps the other
+// parts' products.  Every segment's matrices are dealt round-robin to the
+// parts (all get the same mix of shapes).  Each part is an ordinary batch, so
+// every matrix gets bitwise what it gets alone.  Measured on one box, two
+// runs each, 1 / 2 / 3 / 4 parts: the GPT-2 124M step 1.789-1.795 /
+// 1.732-1.752 / 1.695-1.698 / 1.734-1.741 ms; the 16 extreme-aspect matrices
+// 9.54-9.58 / 9.17-9.19 / 10.58-10.59 / 10.55-10.60 ms.  More parts pay where
+// the prologue is a larger share of the work: its cost grows with the
+// elements, the products' with the elements times the short side m, so K = 3
+// where the batch holds at least 4e-5 elements per nominal flop (m up to about
+// 1000; the 124M set, 5.6e-5), else 2 (the extreme-aspect set, 2.2e-5): then
+// 1.685-1.693 and 9.08-9.13 ms in three runs.  Taken for a batch of one launch
+// group with at least 2 K matrices and 5e11 nominal flops.  MUON_SPLIT=0 turns
+// it off, MUON_SPLIT=2..4 forces K (for tuning).
 constexpr double kSplitMinFlops = 5e11;  // nominal NS5 flops of a batch worth splitting
-struct Halves {
-    std::vector<Segment> segs[2];
-    std::vector<std::vector<const float*>> gs[2];
-    std::vector<std::vector<float*>> os[2], bs[2];
-};
-bool split_pays(const std::vector<Segment>& segs) {
-    static const bool off = [] {
+constexpr double kThreePartsRatio = 4e-5;  // elements per nominal flop from which K = 3
+constexpr int kMaxParts = 4;
+// K forced from the environment (0: not forced; 1: no split)
+int split_parts_forced() {
+    static const int k = [] {
         const char* e = getenv("MUON_SPLIT");
-        return e && atoi(e) == 0;
+        if (!e) return 0;
+        const int v = atoi(e);
+        return v <= 1 ? 1 : (v > kMaxParts ? kMaxParts : v);
     }();
-    if (off) return false;
-    double flops = 0.0;
+    return k;
+}
+struct Parts {
+    int k = 1;
+    std::vector<Segment> segs[kMaxParts];
+    std::vector<std::vector<const float*>> gs[kMaxParts];
+    std::vector<std::vector<float*>> os[kMaxParts], bs[kMaxParts];
+};
+// Parts for a batch (1: no split).
+int split_parts(const std::vector<Segment>& segs) {
+    const int forced = split_parts_forced();
+    if (forced == 1) return 1;
+    double flops = 0.0, elems = 0.0;
     int64_t mats = 0;
     for (const Segment& sg : segs) {
         const double m = static_cast<double>(sg.rows < sg.cols ? sg.rows : sg.cols);
         const double n = static_cast<double>(sg.rows < sg.cols ? sg.cols : sg.rows);
         flops += static_cast<double>(sg.count) * 5.0 * (4.0 * m * m * n + 2.0 * m * m * m);
+        elems += static_cast<double>(sg.count) * m * n;
         mats += sg.count;
     }
-    return mats >= 4 && flops >= kSplitMinFlops;
+    const int k = forced ? forced : (elems >= kThreePartsRatio * flops ? 3 : 2);
+    return (mats >= 2 * k && flops >= kSplitMinFlops) ? k : 1;
 }
-// Deals each segment's matrices to the halves (even positions to the first).
-void split_halves(const std::vector<Segment>& segs, bool ptrs, Halves* h) {
-    for (int half = 0; half < 2; ++half) {
-        h->segs[half].clear();
-        h->gs[half].assign(segs.size(), {});
-        h->os[half].assign(segs.size(), {});
-        h->bs[half].assign(segs.size(), {});
+// Deals each segment's matrices to the k parts (position i to part i mod k).
+void split_parts_of(const std::vector<Segment>& segs, bool ptrs, int k, Parts* pt) {
+    pt->k = k;
+    for (int part = 0; part < k; ++part) {
+        pt->segs[part].clear();
+        pt->gs[part].assign(segs.size(), {});
+        pt->os[part].assign(segs.size(), {});
+        pt->bs[part].assign(segs.size(), {});
     }
     for (size_t q = 0; q < segs.size(); ++q) {
         const Segment& sg = segs[q];
-        for (int half = 0; half < 2; ++half) {
-            const int64_t cnt = (sg.count + 1 - half) / 2;
+        for (int part = 0; part < k; ++part) {
+            const int64_t cnt = sg.count > part ? (sg.count - part + k - 1) / k : 0;
             if (cnt == 0) continue;
             if (ptrs) {
-                for (int64_t i = half; i < sg.count; i += 2) {
-                    h->gs[half][q].push_back(sg.G[i]);
-                    h->os[half][q].push_back(sg.out[i]);
-                    if (sg.buf) h->bs[half][q].push_back(sg.buf[i]);
+                for (int64_t i = part; i < sg.count; i += k) {
+                    pt->gs[part][q].push_back(sg.G[i]);
+                    pt->os[part][q].push_back(sg.out[i]);
+                    if (sg.buf) pt->bs[part][q].push_back(sg.buf[i]);
                 }
             }
-            Segment hs = sg;
-            hs.count = cnt;
-            hs.G = ptrs ? h->gs[half][q].data() : nullptr;
-            hs.out = ptrs ? h->os[half][q].data() : nullptr;
-            hs.buf = (ptrs && sg.buf) ? h->bs[half][q].data() : nullptr;
-            h->segs[half].push_back(hs);
+            Segment ps = sg;
+            ps.count = cnt;
+            ps.G = ptrs ? pt->gs[part][q].data() : nullptr;
+            ps.out = ptrs ? pt->os[part][q].data() : nullptr;
+            ps.buf = (ptrs && sg.buf) ? pt->bs[part][q].data() : nullptr;
+            pt->segs[part].push_back(ps);
         }
     }
 }
-// The plan of a batch: its launch groups, or those of its two halves (the
-// second half's workspace after the first's).  Returns a status.
+// The plan of a batch: its launch groups, or those of its parts (each part's
+// workspace after the previous one's).  Returns a status.
 struct BatchPlan {
-    bool split = false;
-    Halves halves;
-    std::vector<Group> groups[2];
-    size_t off_second = 0, bytes = 0;
+    int parts = 1;
+    Parts split;
+    std::vector<Group> groups[kMaxParts];
+    size_t off[kMaxParts] = {};
+    size_t bytes = 0;
 };
 int plan_batch(const std::vector<Segment>& segs, bool ptrs, bool allow_split, BatchPlan* bp) {
     int st = plan_groups(segs.data(), static_cast<int>(segs.size()), &bp->groups[0]);
     if (st) return st;
     bp->bytes = groups_bytes(bp->groups[0]);
+    bp->parts = 1;
     // (a batch of several launch groups already runs them one after another;
-    // measured, the 1.5B set's two groups lost 0.9% as two halves)
-    bp->split = allow_split && bp->groups[0].size() == 1 && split_pays(segs);
-    if (!bp->split) return MUON_OK;
-    split_halves(segs, ptrs, &bp->halves);
-    for (int half = 0; half < 2; ++half) {
-        st = plan_groups(bp->halves.segs[half].data(), static_cast<int>(bp->halves.segs[half].size()),
-                         &bp->groups[half]);
+    // measured, the 1.5B set's two groups lost 0.9% as two halves and 1.3%
+    // as its two groups on two streams)
+    const int k = allow_split && bp->groups[0].size() == 1 ? split_parts(segs) : 1;
+    if (k < 2) return MUON_OK;
+    bp->parts = k;
+    split_parts_of(segs, ptrs, k, &bp->split);
+    size_t off = 0;
+    for (int part = 0; part < k; ++part) {
+        st = plan_groups(bp->split.segs[part].data(), static_cast<int>(bp->split.segs[part].size()),
+                         &bp->groups[part]);
         if (st) return st;
+        bp->off[part] = off;
+        off = align256(off + groups_bytes(bp->groups[part]));
     }
-    bp->off_second = align256(groups_bytes(bp->groups[0]));
-    bp->bytes = bp->off_second + groups_bytes(bp->groups[1]);
+    bp->bytes = off;
     return MUON_OK;
 }
 
-// The side stream and events of the two-stream schedule, per device, made on
-// first use (default priority; the stream does not synchronise with the
+// The side streams and events of the multi-stream schedule, per device, made
+// on first use (default priority; the streams do not synchronise with the
 // null stream).  Calls that use them enqueue under one lock, since the events
 // are shared.
-struct SideStream {
+struct SideStreams {
     std::once_flag once;
     bool ok = false;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, prologue = nullptr, join = nullptr;
+    hipStream_t stream[kMaxParts] = {};                     // [0] unused (the caller's)
+    hipEvent_t fork = nullptr, prologue[kMaxParts] = {}, join[kMaxParts] = {};
 };
-SideStream g_side[kMaxDevices];
+SideStreams g_side[kMaxDevices];
 std::mutex g_side_lock;
-SideStream* side_stream() {
+SideStreams* side_streams() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         (void)hipGetLastError();
         return nullptr;
     }
-    SideStream* s = &g_side[dev];
+    SideStreams* s = &g_side[dev];
     std::call_once(s->once, [s] {
-        s->ok = hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) == hipSuccess &&
-                hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) == hipSuccess &&
-                hipEventCreateWithFlags(&s->prologue, hipEventDisableTiming) == hipSuccess &&
-                hipEventCreateWithFlags(&s->join, hipEventDisableTiming) == hipSuccess;
-        if (!s->ok) (void)hipGetLastError();
+        bool ok = hipEventCreateWithFlags(&s->fork, hipEventDisableTiming) == hipSuccess;
+        for (int p = 0; p < kMaxParts && ok; ++p) {
+            if (p > 0) ok = hipStreamCreateWithFlags(&s->stream[p], hipStreamNonBlocking) == hipSuccess;
+            ok = ok && hipEventCreateWithFlags(&s->prologue[p], hipEventDisableTiming) == hipSuccess &&
+                 hipEventCreateWithFlags(&s->join[p], hipEventDisableTiming) == hipSuccess;
+        }
+        s->ok = ok;
+        if (!ok) (void)hipGetLastError();
     });
     return s->ok ? s : nullptr;
 }
@@ -854,26 +883,37 @@ int run_batched(const float* const* G, float* const* out, float* const* buf, flo
     st = check_workspace(ws, ws_bytes, bp.bytes);
     if (st) return st;
     char* w = static_cast<char*>(ws);
-    SideStream* side = bp.split ? side_stream() : nullptr;
+    SideStreams* side = bp.parts > 1 ? side_streams() : nullptr;
     if (!side) {
-        // one stream: the halves (when planned) one after the other
-        st = run_groups(bp.groups[0], k, up, mu, steps, eps, w, stream, sink);
-        if (st || !bp.split) return st;
-        return run_groups(bp.groups[1], k, up, mu, steps, eps, w + bp.off_second, stream, nullptr);
+        // one stream: the parts (when planned) one after the other
+        for (int part = 0; part < bp.parts; ++part) {
+            st = run_groups(bp.groups[part], k, up, mu, steps, eps, w + bp.off[part], stream,
+                            part == 0 ? sink : nullptr);
+            if (st) return st;
+        }
+        return ok();
     }
     std::lock_guard<std::mutex> lock(g_side_lock);
     hipError_t e = hipEventRecord(side->fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "side stream fork");
-    st = run_groups(bp.groups[0], k, up, mu, steps, eps, w, stream, nullptr, side->prologue);
-    if (st) return st;
-    e = hipStreamWaitEvent(side->stream, side->prologue, 0);
-    if (e != hipSuccess) return hip_fail(e, "side stream wait");
-    st = run_groups(bp.groups[1], k, up, mu, steps, eps, w + bp.off_second, side->stream, nullptr);
-    if (st) return st;
-    e = hipEventRecord(side->join, side->stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
-    if (e != hipSuccess) return hip_fail(e, "side stream join");
+    for (int part = 0; part < bp.parts; ++part) {
+        hipStream_t s = part == 0 ? stream : side->stream[part];
+        if (part > 0) {
+            // after everything before the call, and after the previous
+            // part's prologue
+            e = hipStreamWaitEvent(s, side->fork, 0);
+            if (e == hipSuccess) e = hipStreamWaitEvent(s, side->prologue[part - 1], 0);
+            if (e != hipSuccess) return hip_fail(e, "side stream wait");
+        }
+        st = run_groups(bp.groups[part], k, up, mu, steps, eps, w + bp.off[part], s, nullptr,
+                        part + 1 < bp.parts ? side->prologue[part] : nullptr);
+        if (st) return st;
+    }
+    for (int part = 1; part < bp.parts; ++part) {
+        e = hipEventRecord(side->join[part], side->stream[part]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join[part], 0);
+        if (e != hipSuccess) return hip_fail(e, "side stream join");
+    }
     return ok();
 }
 

@@ -5,8 +5,8 @@ the same step run eagerly.  Each replay runs from the same momentum buffers
 as an eager step between the replays, with unrelated eager work and
 synchronisations in between, and is checked against that eager step; this
 covers the caller-workspace entry (muon_momentum_ns5_batched, whose batch
-here is large enough to run as two halves on two streams, so the capture
-takes in the library's side stream) and the entry that allocates nothing
+here is large enough to run as three parts on three streams, so the capture
+takes in the library's side streams) and the entry that allocates nothing
 (muon_momentum_ns5_batched_static)."""
 
 import numpy as np
@@ -17,7 +17,8 @@ from newton_schulz_09_amd import step
 
 pytestmark = pytest.mark.gpu
 
-# (5.3e11 nominal flops: the batch runs as two halves on two streams)
+# (5.3e11 nominal flops, 5.7e-5 elements per flop: the batch runs as three
+# parts on three streams)
 SHAPES = [(768, 768), (768, 2304), (3072, 768), (64, 128), (128, 64), (200, 520), (33, 17), (768, 2304)] + \
     [(768, 3072)] * 10
 
