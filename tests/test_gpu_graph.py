@@ -7,13 +7,18 @@ synchronisations in between, and is checked against that eager step; this
 covers the caller-workspace entry (muon_momentum_ns5_batched, whose batch
 here is large enough to run as three parts on three streams, so the capture
 takes in the library's side streams) and the entry that allocates nothing
-(muon_momentum_ns5_batched_static)."""
+(muon_momentum_ns5_batched_static).  The GPT-2 124M step, which the
+benchmark times as graph replays, is checked the same way at its full size,
+and its first replay against the oracle on one matrix of each shape."""
 
 import numpy as np
 import pytest
 import torch
 
-from newton_schulz_09_amd import step
+import oracle
+from newton_schulz_09_amd import step, workloads
+
+from . import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +110,29 @@ def test_static_entry_replays_from_a_graph(muon):
     for k in range(len(gs)):
         assert torch.equal(outs[k], want[k]), k
         assert torch.equal(bs[k], ref_b[k]), k
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_124m_step_replays_from_a_graph(muon):
+    """The benchmark's configuration: the 48-matrix GPT-2 124M step captured
+    once and replayed; every replay bitwise equals the eager step from the
+    same buffers, and the first replay's updates of one matrix per shape
+    match the oracle (momentum within 1 float32 ulp)."""
+    items = workloads.gpt2_124m()
+    st = step.MuonStep([it[2].shape for it in items])
+    for k, (_, _, G, buf) in enumerate(items):
+        st.grads[k].copy_(torch.from_numpy(G))
+        st.bufs[k].copy_(torch.from_numpy(buf))
+    bufs0 = [b.clone() for b in st.bufs]
+    graph = _capture(st.fused_step)
+    for b, b0 in zip(st.bufs, bufs0):
+        b.copy_(b0)
+    graph.replay()
+    torch.cuda.synchronize()
+    for k in range(4):  # one matrix of each shape (the layer-0 block)
+        _, _, G, buf = items[k]
+        want_b, want_u = oracle.momentum_nesterov(G, buf, 0.95)
+        assert parity.ulp_diff32(parity.to_np(st.bufs[k]), want_b).max() <= 1
+        r = parity.assert_ns5_parity(parity.to_np(st.outs[k]), oracle.ns5(want_u), f"replay, {G.shape}")
+        print(f"gpt2-124m replay {G.shape}: relative Frobenius {r:.3g}", flush=True)
+    _replays_match_eager(st.fused_step, graph.replay, st.bufs, bufs0, st.outs, "gpt2-124m")
