@@ -92,8 +92,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "57795141fc3d25bba86aa7365c9659ae0bb453554fe07b65b5a2f01c45879d38",
-    "fetch_bytes": 285905603,
+    "sources_sha256": "130f1c836020951ebb0c219c800da082472a21094403613396d1cbf2a56e2ff8",
+    "fetch_bytes": 285794276,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
