@@ -46,6 +46,7 @@ tiles only, so the second is the closer measure of the matrix cores' work.
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -68,7 +69,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--skip-cpu-baseline", action="store_true")
     p.add_argument("--skip-square", action="store_true", help="skip the 4096x4096 NS5 line")
     p.add_argument("--skip-extras", action="store_true", help="only the timed step (for profiling)")
@@ -282,8 +283,21 @@ def _rates(nominal, symmin, ms):
             "pct_mfma_peak_symmetric_min": round(100 * tf_min / PEAK_BF16_TFLOPS, 2)}
 
 
-def _timed(torch, fn, reps, warm=2):
+def _timed(torch, fn, reps, warm=2, settle_ms=100.0):
+    """Mean ms per call of `fn` over `reps` calls, after an untimed warm-up
+    of at least `warm` calls and `settle_ms` of GPU time: the clocks take some
+    tens of ms of matrix work to settle after other work or idle time (one
+    4096^2 NS5 measured 1.55 ms over its first 10 calls, 1.41 ms from the
+    20th on)."""
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
     for _ in range(warm):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    per_call = start.elapsed_time(stop) / max(warm, 1)
+    for _ in range(math.ceil(max(0.0, settle_ms - per_call * warm) / max(per_call, 1e-3))):
         fn()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -482,7 +496,8 @@ def main():
     eager_ms = time_step(st.fused_step, args.steps, torch)
     log(f"step, called from the host: {eager_ms:.4f} ms")
     graph = capture_step(st, torch)
-    graph.replay()
+    for _ in range(args.warmup):
+        graph.replay()
     ms = time_step(graph.replay, args.steps, torch)
     flops = st.nominal_ns5_flops()
     value = flops / (ms * 1e-3) / 1e12
