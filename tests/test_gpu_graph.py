@@ -4,12 +4,13 @@ never by memset nodes), so a captured step replays to bitwise the results of
 the same step run eagerly.  Each replay runs from the same momentum buffers
 as an eager step between the replays, with unrelated eager work and
 synchronisations in between, and is checked against that eager step; this
-covers the caller-workspace entry (muon_momentum_ns5_batched, whose batch
-here is large enough to run as three parts on three streams, so the capture
-takes in the library's side streams) and the entry that allocates nothing
-(muon_momentum_ns5_batched_static).  The GPT-2 124M step, which the
-benchmark times as graph replays, is checked the same way at its full size,
-and its first replay against the oracle on one matrix of each shape."""
+covers the caller-workspace entry (muon_momentum_ns5_batched; the mixed set
+below runs as several launch groups on the caller's stream) and the entry
+that allocates nothing (muon_momentum_ns5_batched_static).  The GPT-2 124M step, which the
+benchmark times as graph replays, is checked the same way at its full size
+(it runs as three parts on three streams, so the capture takes in the
+library's side streams), and its first replay against the oracle on one
+matrix of each shape."""
 
 import numpy as np
 import pytest
@@ -22,8 +23,7 @@ from . import parity
 
 pytestmark = pytest.mark.gpu
 
-# (5.3e11 nominal flops, 5.7e-5 elements per flop: the batch runs as three
-# parts on three streams)
+# (tile-64 and tile-128 shapes: several launch groups, one stream)
 SHAPES = [(768, 768), (768, 2304), (3072, 768), (64, 128), (128, 64), (200, 520), (33, 17), (768, 2304)] + \
     [(768, 3072)] * 10
 

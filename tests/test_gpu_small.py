@@ -551,6 +551,44 @@ def test_two_4096_matrices_equal_single_calls(muon):
         assert torch.isfinite(outs[k]).all()
 
 
+# Batches the library runs as several parts on several streams (one launch
+# group, at least 5e11 nominal flops), with segments that the parts cannot
+# share evenly (tests/test_split_plan.py checks on the CPU that these batches
+# are split and how).
+SPLIT_BATCHES = {
+    # 20 matrices of the 768 class, 7.6e11 nominal flops, 5.7e-5 elements per
+    # flop: three parts; segments of 13, 5 and 2 go 5/4/4, 2/2/1 and 1/1/0
+    "three-parts-uneven": [(768, 3072)] * 13 + [(3072, 768)] * 5 + [(768, 768)] * 2,
+    # five 2048^2 matrices, 1.3e12 nominal flops, 1.6e-5 elements per flop:
+    # two parts of 3 and 2
+    "two-parts-uneven": [(2048, 2048)] * 5,
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_BATCHES))
+def test_split_batches_equal_single_calls(muon, name):
+    """The fused step over a batch that runs as parts on several streams:
+    every matrix's update and new momentum buffer are bitwise what a call on
+    that matrix alone gives, and a second call gives the same again."""
+    shapes = SPLIT_BATCHES[name]
+    rng = np.random.default_rng(91)
+    host_g = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    host_b = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    Gs = [cuda(h) for h in host_g]
+    bufs = [cuda(h) for h in host_b]
+    outs = muon.ns5_batched(Gs, bufs=bufs, mu=0.95)
+    bufs2 = [cuda(h) for h in host_b]
+    again = muon.ns5_batched(Gs, bufs=bufs2, mu=0.95)
+    torch.cuda.synchronize()
+    for k, G in enumerate(Gs):
+        assert torch.equal(outs[k], again[k]) and torch.equal(bufs[k], bufs2[k]), f"{name}: matrix {k} differs between calls"
+        b = cuda(host_b[k])
+        o = muon.ns5_batched([G], bufs=[b], mu=0.95)[0]
+        assert torch.equal(o, outs[k]), f"{name}: update {k} {tuple(G.shape)} differs from its single call"
+        assert torch.equal(b, bufs[k]), f"{name}: buffer {k} {tuple(G.shape)} differs from its single call"
+        assert torch.isfinite(o).all().item(), k
+
+
 @pytest.mark.parametrize("shapes", [
     # 16 x 36 upper 256 tiles in X X^T and b A + c A A (2.25 rounds of 256
     # CUs); alone, a 2048^2 matrix takes 192 tiles for them
