@@ -78,9 +78,10 @@ typedef enum muon_dtype {
 #define MUON_NS5_MAX_LONG (1 << 20)
 
 /*
- * Nesterov momentum, one step (summary paragraph of the Muon section:
- * Nesterov momentum in the update; its formula did not survive in the page,
- * and the plain SGD-Nesterov form without dampening is used):
+ * Nesterov momentum, one step (summary paragraph of the Muon section, which
+ * names Nesterov momentum as the first stage of the update but whose formula
+ * did not survive in the page; the plain SGD-Nesterov form without dampening
+ * is used):
  *     buf[i] <- mu * buf[i] + g[i]
  *     u[i]   <- g[i] + mu * buf[i]          (new buf)
  * each computed as one float32 fused multiply-add (one rounding).

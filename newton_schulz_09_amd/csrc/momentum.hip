@@ -1,6 +1,6 @@
 // Nesterov momentum (summary paragraph of the Muon section in the Synced
-// report on Modded-NanoGPT: Nesterov momentum in the update, orthogonalised
-// afterwards).  Reading of the lost formula: buf <- mu*buf + g ;
+// report on Modded-NanoGPT: the gradient first passes through Nesterov
+// momentum, and the resulting direction is what gets orthogonalised).  Reading of the lost formula: buf <- mu*buf + g ;
 // u <- g + mu*buf, each a single float32 fused multiply-add.
 //
 // HBM-bound streaming kernel: 16 bytes per element (read g and buf, write buf

@@ -1,6 +1,6 @@
 """Pins for the oracle's Nesterov momentum (Muon section of the Synced report
-on Modded-NanoGPT, summary paragraph: Nesterov momentum, orthogonalise after
-it).  Reading: buf <- mu*buf + g, u <- g + mu*buf, one float32 rounding per
+on Modded-NanoGPT, summary paragraph, where the momentum output is the
+matrix that gets orthogonalised).  Reading: buf <- mu*buf + g, u <- g + mu*buf, one float32 rounding per
 result.  Pinned by closed forms of the linear recurrence and exact arithmetic."""
 
 from fractions import Fraction
