@@ -771,7 +771,11 @@ int split_parts(const std::vector<Segment>& segs) {
     const int k = forced ? forced : (elems >= kThreePartsRatio * flops ? 3 : 2);
     return (mats >= 2 * k && flops >= kSplitMinFlops) ? k : 1;
 }
-// Deals each segment's matrices to the k parts (position i to part i mod k).
+// Deals the matrices to the k parts round-robin, in segment order and
+// without restarting at each segment: matrix i of a segment goes to part
+// (s + i) mod k, s being the number of matrices in the segments before it
+// (mod k).  Each segment is shared as evenly as it can be, and every part
+// gets at least floor(count / k) matrices.
 void split_parts_of(const std::vector<Segment>& segs, bool ptrs, int k, Parts* pt) {
     pt->k = k;
     for (int part = 0; part < k; ++part) {
@@ -780,13 +784,15 @@ void split_parts_of(const std::vector<Segment>& segs, bool ptrs, int k, Parts* p
         pt->os[part].assign(segs.size(), {});
         pt->bs[part].assign(segs.size(), {});
     }
+    int start = 0;  // the part that takes the segment's first matrix
     for (size_t q = 0; q < segs.size(); ++q) {
         const Segment& sg = segs[q];
         for (int part = 0; part < k; ++part) {
-            const int64_t cnt = sg.count > part ? (sg.count - part + k - 1) / k : 0;
+            const int64_t first = (part - start + k) % k;  // the segment's first matrix in this part
+            const int64_t cnt = sg.count > first ? (sg.count - first + k - 1) / k : 0;
             if (cnt == 0) continue;
             if (ptrs) {
-                for (int64_t i = part; i < sg.count; i += k) {
+                for (int64_t i = first; i < sg.count; i += k) {
                     pt->gs[part][q].push_back(sg.G[i]);
                     pt->os[part][q].push_back(sg.out[i]);
                     if (sg.buf) pt->bs[part][q].push_back(sg.buf[i]);
@@ -799,6 +805,7 @@ void split_parts_of(const std::vector<Segment>& segs, bool ptrs, int k, Parts* p
             ps.buf = (ptrs && sg.buf) ? pt->bs[part][q].data() : nullptr;
             pt->segs[part].push_back(ps);
         }
+        start = static_cast<int>((start + sg.count) % k);
     }
 }
 // The plan of a batch: its launch groups, or those of its parts (each part's

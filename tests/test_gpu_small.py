@@ -557,8 +557,11 @@ def test_two_4096_matrices_equal_single_calls(muon):
 # are split and how).
 SPLIT_BATCHES = {
     # 20 matrices of the 768 class, 7.6e11 nominal flops, 5.7e-5 elements per
-    # flop: three parts; segments of 13, 5 and 2 go 5/4/4, 2/2/1 and 1/1/0
+    # flop: three parts; segments of 13, 5 and 2 go 5/4/4, 1/2/2 and 1/1/0
     "three-parts-uneven": [(768, 3072)] * 13 + [(3072, 768)] * 5 + [(768, 768)] * 2,
+    # eight shapes of one matrix each, 5.9e11 nominal flops: three parts of
+    # 3, 3 and 2 (the round-robin runs on across segments)
+    "three-parts-one-per-shape": [(768, n) for n in range(4096, 8192, 512)],
     # five 2048^2 matrices, 1.3e12 nominal flops, 1.6e-5 elements per flop:
     # two parts of 3 and 2
     "two-parts-uneven": [(2048, 2048)] * 5,

@@ -1,5 +1,6 @@
 """The host planner's multi-stream split, without a GPU: the workspace query
-includes the parts' layouts when a batch is split, so its size tells whether
+includes the parts' layouts when a batch is split, so where the parts' tile
+choices or alignment differ from the whole batch's, its size tells whether
 the library splits a batch.  Each case runs in a child process, since
 MUON_SPLIT is read once per process."""
 
