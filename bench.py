@@ -93,8 +93,8 @@ COPY_BYTES = 1 << 30
 # reported as null once their hash differs (the summary is
 # profiles/gpt2_124m_step_traffic.md).
 TRAFFIC = {
-    "sources_sha256": "130f1c836020951ebb0c219c800da082472a21094403613396d1cbf2a56e2ff8",
-    "fetch_bytes": 285794276,
+    "sources_sha256": "fa68d28e76402f24928003fafb0bbf7ef92c7276917ecf32dc902f64bbb751fd",
+    "fetch_bytes": 285486195,
     "write_bytes": 169869312,
 }
 TRAFFIC_SOURCES = ("newton_schulz_09_amd/csrc/gemm.hip", "newton_schulz_09_amd/csrc/api.hip",
