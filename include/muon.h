@@ -25,6 +25,9 @@
  *    anything enqueued after it; this holds under graph capture too.
  *    Results do not depend on the split.  Batched calls enqueue under a
  *    process-wide lock.
+ *  - Matrices whose short side is at most 64 and long side at most 256 run
+ *    their whole step in one launch (one workgroup per matrix) in every
+ *    entry point; the workspace sizes keep their share, unused.
  *  - Arguments are validated before anything is enqueued; a validation error
  *    returns a non-zero status and enqueues nothing.  A HIP launch error is
  *    reported as MUON_ERR_HIP; faults during execution surface at the

@@ -14,7 +14,8 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "momentum.hip", "norm_cast.hip", "gemm.hip", "f32_iter.hip", "static_ws.hip", "polar_svd.hip"]
+SOURCES = ["api.hip", "momentum.hip", "norm_cast.hip", "gemm.hip", "f32_iter.hip", "static_ws.hip", "polar_svd.hip",
+           "small.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed-fp32 instructions are kept out of the generated code

@@ -266,9 +266,13 @@ struct Chunk {
 
 // Chunks that share the tile size: each GEMM of each NS5 step is a single
 // launch over all of them.  Groups run one after another, each reusing the
-// workspace from its start.
+// workspace from its start.  A small group holds matrices of the small range
+// (short side <= kSmallM, long side <= kSmallN): each of its chunks is one
+// launch that runs the whole step in LDS (its workspace share is reserved
+// but not used).
 struct Group {
     std::vector<Chunk> chunks;
+    bool small = false;
     int tile = 0;
     int mats = 0;
     int64_t bx_blocks = 0;  // workgroups of the largest launch (a X + B X)
@@ -302,13 +306,15 @@ int plan_groups(const Segment* segs, int nseg, std::vector<Group>* groups, size_
                 if (fit >= pl.cnt) fit = pl.cnt - 1;
                 make_plan(sg.rows, sg.cols, fit < 1 ? 1 : fit, &pl);
             }
+            const bool small = pl.m <= kSmallM && pl.n <= kSmallN;
             Group* g = groups->empty() ? nullptr : &groups->back();
-            if (!g || g->tile != pl.tile || g->chunks[0].plan.sym_tile != pl.sym_tile ||
+            if (!g || g->small != small || g->tile != pl.tile || g->chunks[0].plan.sym_tile != pl.sym_tile ||
                 g->mats + pl.cnt > kMaxGroup || (cap > 0 && g->bytes + pl.bytes > cap) ||
                 static_cast<int>(g->chunks.size()) == kMaxSeg || g->bx_blocks + bx_blocks(pl) > kMaxWorkgroups) {
                 groups->emplace_back();
                 g = &groups->back();
                 g->tile = pl.tile;
+                g->small = small;
             }
             Chunk c;
             c.G = sg.G ? sg.G + start : nullptr;
@@ -384,6 +390,47 @@ int run_groups(const std::vector<Group>& groups, const Coeffs& k, const Update& 
                EventSink* sink, hipEvent_t after_prologue = nullptr) {
     (void)hipGetLastError();  // start from a clean error state
     for (const Group& grp : groups) {
+        if (grp.small) {  // one launch: a workgroup per matrix, every chunk a segment
+            SmallArgs sa{};
+            sa.nseg = static_cast<int>(grp.chunks.size());
+            sa.steps = steps;
+            sa.apply = up.apply ? 1 : 0;
+            sa.mu = mu;
+            sa.eps = eps;
+            sa.a = k.a;
+            sa.b = k.b;
+            sa.c = k.c;
+            sa.lr = up.lr;
+            ConstPtrTable gt{};
+            PtrTable ot{}, bt{};
+            const bool fused = grp.chunks[0].buf != nullptr;  // the same for every chunk of a call
+            int at = 0;
+            for (int ci = 0; ci < sa.nseg; ++ci) {
+                const Chunk& c = grp.chunks[ci];
+                const Ns5Plan& pl = c.plan;
+                SmallSeg& sg = sa.seg[ci];
+                sg.first = at;
+                sg.cnt = pl.cnt;
+                sg.rows = static_cast<int>(pl.rows);
+                sg.cols = static_cast<int>(pl.cols);
+                sg.m = pl.m;
+                sg.n = pl.n;
+                sg.np = static_cast<int>(round_up(pl.n, 32));
+                sg.tall = pl.tall ? 1 : 0;
+                for (int i = 0; i < pl.cnt; ++i, ++at) {
+                    gt.p[at] = c.G[i];
+                    ot.p[at] = c.out[i];
+                    if (fused) bt.p[at] = c.buf[i];
+                }
+            }
+            hipError_t e = launch_ns5_small(sa, gt, ot, fused ? &bt : nullptr, up.bf16_io, stream);
+            if (e != hipSuccess) return hip_fail(e, "small-matrix launch");
+            if (after_prologue && &grp == &groups.front()) {
+                hipError_t e = hipEventRecord(after_prologue, stream);
+                if (e != hipSuccess) return hip_fail(e, "event record");
+            }
+            continue;
+        }
         const int nseg = static_cast<int>(grp.chunks.size());
         PtrTable out_all{};
         int out_base[kMaxSeg];

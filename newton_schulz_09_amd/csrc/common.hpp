@@ -60,4 +60,14 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double d) {
     return static_cast<bf16_t>(__float_as_uint(f) >> 16);
 }
 
+// The float32 quotient q (within ~2 ulps of the exact one) cannot be rounded
+// to bf16 directly: it lies within 8 ulps of a bf16 rounding midpoint, or is
+// not a normal float32 (zero excepted).
+__device__ __forceinline__ bool cast_needs_f64(float q) {
+    const uint32_t bits = __float_as_uint(q);
+    const uint32_t mag = bits & 0x7fffffffu;
+    const bool near_mid = ((bits & 0xffffu) - 0x7ff8u) <= 16u;
+    return near_mid || (mag != 0u && mag < 0x01000000u) || mag >= 0x7f800000u;
+}
+
 }  // namespace muon

@@ -184,6 +184,27 @@ hipError_t launch_zero_rows(bf16_t* X, int64_t x_mat, int cnt, int first_row, in
 hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const PtrTable& out, hipStream_t stream,
                            bool apply = false, float lr = 0.0f, bool out16 = false);
 
+// The whole NS5 (or Muon step) of small matrices, short side up to kSmallM
+// and long side up to kSmallN, one workgroup per matrix with everything in
+// LDS (small.hip), one launch over up to kMaxSeg segments of same-shaped
+// matrices: segment q covers entries [first, first + cnt) of the pointer
+// tables.  np is n rounded up to 32.  buf: the fused Muon step (float32
+// only); io16: G and the outputs hold bfloat16 (pure NS5); apply: p <- p - lr
+// * O into out.
+constexpr int kSmallM = 64;
+constexpr int kSmallN = 256;
+struct SmallSeg {
+    int first, cnt;
+    int rows, cols, m, n, np, tall;
+};
+struct SmallArgs {
+    SmallSeg seg[kMaxSeg];
+    int nseg, steps, apply;
+    float mu, eps, a, b, c, lr;
+};
+hipError_t launch_ns5_small(const SmallArgs& s, const ConstPtrTable& G, const PtrTable& out, const PtrTable* buf,
+                            bool io16, hipStream_t stream);
+
 // One GEMM launch of `blocks` workgroups with tile x tile_n output tiles:
 // square tiles of 64, 128 or 256 for every kind, and 256 x 128 or 192 x 256
 // for a X + B X.

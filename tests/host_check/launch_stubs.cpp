@@ -126,6 +126,33 @@ hipError_t launch_copy_out(const Ns5Plan& plan, int cnt, const bf16_t* X, const 
     return hipSuccess;
 }
 
+// The small-matrix launch reads G, writes out (and buf) only: every
+// segment's shape must fit the kernel's LDS tiles, the segments must tile
+// the pointer tables in order, and every pointer used must be set.
+hipError_t launch_ns5_small(const SmallArgs& s, const ConstPtrTable& G, const PtrTable& out, const PtrTable* buf,
+                            bool io16, hipStream_t) {
+    if (s.nseg < 1 || s.nseg > kMaxSeg) die("small segments", s.nseg, 0);
+    if (io16 && (buf || s.apply)) die("small bf16 with momentum or update", 0, 0);
+    int total = 0;
+    for (int q = 0; q < s.nseg; ++q) {
+        const SmallSeg& sg = s.seg[q];
+        if (sg.first != total || sg.cnt < 1) die("small segment table", sg.first, total);
+        if (sg.m < 1 || sg.m > kSmallM || sg.n < sg.m || sg.n > kSmallN) die("small shape", sg.m, sg.n);
+        if (sg.np % 32 != 0 || sg.np < sg.n || sg.np > kSmallN) die("small padded width", sg.np, sg.n);
+        if (static_cast<long long>(sg.rows) * sg.cols != static_cast<long long>(sg.m) * sg.n)
+            die("small extent", sg.rows, sg.cols);
+        if ((sg.rows > sg.cols) != (sg.tall != 0)) die("small orientation", sg.rows, sg.cols);
+        total += sg.cnt;
+    }
+    if (total > kMaxGroup) die("small pointer table", total, kMaxGroup);
+    for (int i = 0; i < total; ++i) {
+        if (!G.p[i] || !out.p[i]) die("small null pointer", i, 0);
+        if (buf && !buf->p[i]) die("small null buffer", i, 0);
+    }
+    ++hostcheck::launches;
+    return hipSuccess;
+}
+
 hipError_t launch_gemm(GemmKind kind, int tile, int tile_n, const GemmLaunch& L, int blocks, const PtrTable* out,
                        hipStream_t) {
     const bool sym = kind == GEMM_SYRK || kind == GEMM_AAB;
