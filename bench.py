@@ -28,7 +28,7 @@ Printed (one JSON line on stdout):
                  (muon_newton_schulz_f32_batched), against the float32 matrix
                  peak, and its time over the bf16 NS5 of the same matrices
   single_64x128  one 64x128 Muon step (momentum + NS5) and its 128x64
-                 transpose, microseconds per call (launch-bound)
+                 transpose, microseconds per call (one launch each)
   gpt2_1p5b      the GPT-2 1.5B hidden set (192 matrices, 48 layers x 1600x4800,
                  1600x1600, 1600x6400, 6400x1600), one fused Muon step
   extreme_aspect eight 2048x8192 and eight 8192x2048 matrices, one batched NS5
