@@ -551,6 +551,32 @@ def test_two_4096_matrices_equal_single_calls(muon):
         assert torch.isfinite(outs[k]).all()
 
 
+# The one-launch path of small matrices at the edges of its range (short side
+# up to 64, long side up to 256: four 32-wide blocks of X per wave at 256) and
+# just past them (the tiled path), in one batch and one by one.
+SMALL_EDGE_SHAPES = [(64, 256), (256, 64), (33, 250), (1, 256), (64, 225), (64, 257), (65, 256), (2, 1)]
+
+
+def test_small_range_edges(muon):
+    rng = np.random.default_rng(2024)
+    host = [rng.standard_normal(sh).astype(np.float32) for sh in SMALL_EDGE_SHAPES]
+    bufs = [(0.1 * rng.standard_normal(sh)).astype(np.float32) for sh in SMALL_EDGE_SHAPES]
+    Gs = [cuda(h) for h in host]
+    bd = [cuda(b) for b in bufs]
+    outs = muon.ns5_batched(Gs, bufs=bd, mu=0.95)
+    torch.cuda.synchronize()
+    for k, sh in enumerate(SMALL_EDGE_SHAPES):
+        b1 = cuda(bufs[k])
+        single = muon.ns5_batched([Gs[k]], bufs=[b1], mu=0.95)[0]
+        assert torch.equal(single, outs[k]) and torch.equal(b1, bd[k]), f"{sh}: batched differs from single"
+        want_b, want_u = oracle.momentum_nesterov(host[k], bufs[k], 0.95)
+        assert parity.ulp_diff32(parity.to_np(bd[k]), want_b).max() <= 1, sh
+        got = parity.to_np(outs[k])
+        bar = parity.model_bar(want_u) if want_u.size <= 20000 else (parity.REL_FRO_TOL, parity.SIGMA_TOL)
+        parity.assert_ns5_parity(got, oracle.ns5(want_u), f"{sh}", check_sigma=min(sh) > 1, bar=bar)
+        assert parity.is_bf16_valued(got)
+
+
 # Batches the library runs as several parts on several streams (one launch
 # group, at least 5e11 nominal flops), with segments that the parts cannot
 # share evenly (tests/test_split_plan.py checks on the CPU that these batches
