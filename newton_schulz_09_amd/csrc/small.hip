@@ -7,7 +7,8 @@
 // Such a matrix leaves nearly all of the GPU idle in the tiled path, which
 // spends its time in the 17 launches of a step (momentum + norm, cast, three
 // products per NS5 step); here the call is one launch of one workgroup per
-// matrix.  The arithmetic and its rounding points are those of the tiled
+// matrix, of 8 waves (two per SIMD, so that one hides the other's
+// latencies).  The arithmetic and its rounding points are those of the tiled
 // path: momentum as two float32 fused multiply-adds, the sum of squares of u
 // in float64, X0 = bf16(bf16(u) / (||u|| + eps)) with the quotient in
 // float64, products on the 32 x 32 x 16 bf16 matrix cores with float32
@@ -21,6 +22,7 @@ namespace muon {
 
 namespace {
 
+constexpr int kST = 512;  // threads per workgroup: 8 waves, two per SIMD
 constexpr int kLdx = kSmallN + 8;  // X row stride (elements): 16-byte aligned rows
 constexpr int kLdt = kSmallM + 8;  // X^T, A and B row stride
 
@@ -103,12 +105,12 @@ __device__ __forceinline__ void sym_product(const bf16_t* P, int ldp, int K, con
 }
 
 template <bool MOM, bool IO16>
-__global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTable G, PtrTable OUT, PtrTable BUF) {
+__global__ __launch_bounds__(kST) void k_ns5_small(SmallArgs s, ConstPtrTable G, PtrTable OUT, PtrTable BUF) {
     __shared__ __attribute__((aligned(16))) bf16_t X[kSmallM * kLdx];   // m x n (64 x np used)
     __shared__ __attribute__((aligned(16))) bf16_t XT[kSmallN * kLdt];  // n x m
     __shared__ __attribute__((aligned(16))) bf16_t A[kSmallM * kLdt];
     __shared__ __attribute__((aligned(16))) bf16_t B[kSmallM * kLdt];
-    __shared__ double red[kThreads / 64];
+    __shared__ double red[kST / 64];
     const int mat = static_cast<int>(blockIdx.x), tid = static_cast<int>(threadIdx.x);
     // (the wave index read as uniform, so that branches on it stay scalar)
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,8 +123,8 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
     const bool tall = sg.tall != 0;
 
     // padding rows and columns are zero and stay zero through the iteration
-    for (int i = tid; i < kSmallM * kLdx / 8; i += kThreads) reinterpret_cast<u32x4s*>(X)[i] = u32x4s{0, 0, 0, 0};
-    for (int i = tid; i < kSmallN * kLdt / 8; i += kThreads) reinterpret_cast<u32x4s*>(XT)[i] = u32x4s{0, 0, 0, 0};
+    for (int i = tid; i < kSmallM * kLdx / 8; i += kST) reinterpret_cast<u32x4s*>(X)[i] = u32x4s{0, 0, 0, 0};
+    for (int i = tid; i < kSmallN * kLdt / 8; i += kST) reinterpret_cast<u32x4s*>(XT)[i] = u32x4s{0, 0, 0, 0};
     __syncthreads();
 
     // momentum (fused step), bf16(u) staged in X in the iteration's
@@ -139,12 +141,12 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
                      (!MOM || (reinterpret_cast<uintptr_t>(buf) & 15u) == 0);
     if (vec) {
         const int n4 = numel / 4;
-        RowCol rc(4 * tid, 4 * kThreads, cols);
-        for (int v0 = tid; v0 < n4; v0 += kU * kThreads) {
+        RowCol rc(4 * tid, 4 * kST, cols);
+        for (int v0 = tid; v0 < n4; v0 += kU * kST) {
             f32x4 gv[kU], bv[kU];
 #pragma unroll
             for (int q = 0; q < kU; ++q) {
-                const int i4 = v0 + q * kThreads;
+                const int i4 = v0 + q * kST;
                 if (i4 < n4) {
                     gv[q] = reinterpret_cast<const f32x4*>(g)[i4];
                     if constexpr (MOM) bv[q] = reinterpret_cast<const f32x4*>(buf)[i4];
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
             }
 #pragma unroll
             for (int q = 0; q < kU; ++q) {
-                const int i4 = v0 + q * kThreads;
+                const int i4 = v0 + q * kST;
                 if (i4 < n4) {
                     f32x4 bn;
 #pragma unroll
@@ -171,12 +173,12 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
             }
         }
     }
-    RowCol rc(tid, kThreads, cols);
-    for (int e0 = vec ? numel : tid; e0 < numel; e0 += kU * kThreads) {
+    RowCol rc(tid, kST, cols);
+    for (int e0 = vec ? numel : tid; e0 < numel; e0 += kU * kST) {
         float gv[kU], bv[kU];
 #pragma unroll
         for (int q = 0; q < kU; ++q) {
-            const int e = e0 + q * kThreads;
+            const int e = e0 + q * kST;
             gv[q] = 0.0f;
             bv[q] = 0.0f;
             if (e < numel) {
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
         }
 #pragma unroll
         for (int q = 0; q < kU; ++q) {
-            const int e = e0 + q * kThreads;
+            const int e = e0 + q * kST;
             if (e < numel) {
                 float u = gv[q];
                 if constexpr (MOM) {
@@ -209,15 +211,15 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
     __syncthreads();
     double total = 0.0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) total += red[w];
+    for (int w = 0; w < kST / 64; ++w) total += red[w];
     const double d = sqrt(total) + static_cast<double>(s.eps);
     const float r32 = static_cast<float>(1.0 / d);
     const bool fast_ok = r32 >= 0x1p-126f && r32 <= 0x1.fffffep127f;
     // X0 = bf16(bf16(u) / d), the quotient in float64 and rounded once;
     // four elements per pass, so that their divisions overlap
     {
-        RowCol ij(tid, kThreads, n);
-        for (int e0 = tid; e0 < m * n; e0 += 4 * kThreads) {
+        RowCol ij(tid, kST, n);
+        for (int e0 = tid; e0 < m * n; e0 += 4 * kST) {
             int ii[4], jj[4];
             double q[4];
 #pragma unroll
@@ -225,11 +227,11 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
                 ii[t] = ij.r;
                 jj[t] = ij.c;
                 ij.next();
-                q[t] = e0 + t * kThreads < m * n ? static_cast<double>(bf16_to_f32(X[ii[t] * kLdx + jj[t]])) : 0.0;
+                q[t] = e0 + t * kST < m * n ? static_cast<double>(bf16_to_f32(X[ii[t] * kLdx + jj[t]])) : 0.0;
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                if (e0 + t * kThreads < m * n) {
+                if (e0 + t * kST < m * n) {
                     // q = v fl32(1/d) rounds like v / d unless it lies near a
                     // bf16 rounding midpoint (the cast kernel's criterion)
                     const float q32 = static_cast<float>(q[t]) * r32;
@@ -250,10 +252,10 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
         __syncthreads();
         // X' = B X + a X: block q of X' on wave q mod 4, K = 64 (B's rows and
         // columns past m are zero)
-        f32x16 acc[4];
+        f32x16 acc[16 / (kST / 64)];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int q = wave + 4 * t;
+        for (int t = 0; t < 16 / (kST / 64); ++t) {
+            const int q = wave + (kST / 64) * t;
             if (q < nblk) {
                 const int bi = q / nbj, bj = q - bi * nbj;
                 const bf16_t* pa = B + (32 * bi + (lane & 31)) * kLdt + 8 * (lane >> 5);
@@ -272,8 +274,8 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
         }
         __syncthreads();  // every wave is done reading X, X^T and B
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int q = wave + 4 * t;
+        for (int t = 0; t < 16 / (kST / 64); ++t) {
+            const int q = wave + (kST / 64) * t;
             if (q < nblk) {
                 const int bi = q / nbj, bj = q - bi * nbj;
 #pragma unroll
@@ -292,8 +294,8 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
     float* o = OUT.p[mat];
     const bool ovec = !IO16 && (cols & 3) == 0 && (reinterpret_cast<uintptr_t>(o) & 15u) == 0;
     if (ovec) {
-        RowCol oc4(4 * tid, 4 * kThreads, cols);
-        for (int v0 = tid; v0 < numel / 4; v0 += kThreads, oc4.next()) {
+        RowCol oc4(4 * tid, 4 * kST, cols);
+        for (int v0 = tid; v0 < numel / 4; v0 += kST, oc4.next()) {
             f32x4 w;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void k_ns5_small(SmallArgs s, ConstPtrTab
             *dst = w;
         }
     }
-    RowCol oc(tid, kThreads, cols);
-    for (int e = ovec ? numel : tid; e < numel; e += kThreads, oc.next()) {
+    RowCol oc(tid, kST, cols);
+    for (int e = ovec ? numel : tid; e < numel; e += kST, oc.next()) {
         const int r = oc.r, c = oc.c;
         const bf16_t h = tall ? XT[r * kLdt + c] : X[r * kLdx + c];
         if constexpr (IO16) {
@@ -336,11 +338,11 @@ hipError_t launch_ns5_small(const SmallArgs& s, const ConstPtrTable& G, const Pt
     if (total > kMaxGroup) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(total));
     if (buf)
-        k_ns5_small<true, false><<<grid, kThreads, 0, stream>>>(s, G, out, *buf);
+        k_ns5_small<true, false><<<grid, kST, 0, stream>>>(s, G, out, *buf);
     else if (io16)
-        k_ns5_small<false, true><<<grid, kThreads, 0, stream>>>(s, G, out, PtrTable{});
+        k_ns5_small<false, true><<<grid, kST, 0, stream>>>(s, G, out, PtrTable{});
     else
-        k_ns5_small<false, false><<<grid, kThreads, 0, stream>>>(s, G, out, PtrTable{});
+        k_ns5_small<false, false><<<grid, kST, 0, stream>>>(s, G, out, PtrTable{});
     return hipGetLastError();
 }
 
